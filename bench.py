@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the shared-round attention hot path on one MI355X.
+
+Default workload: 16 one-row decode streams, 32 query / 8 kv heads, head dim
+128, key counts uniform in [512, 4096] in 32-token pages scattered over a
+4096-page pool, split-K 512 keys a partial + merge.  One step = tf_attn_rows
++ tf_attn_merge over every stream (workloads with logits add tf_argmax).
+
+Inputs are resident in HBM before timing starts.  The K/V pool is kept in
+``--copies`` copies (each with its own segment table) and the steps rotate
+over them, so that K/V is read from HBM and not from the 256 MB Infinity
+Cache.  Printed: one JSON line (metric, value = KV-read GB/s of the whole
+step, roofline of the rows kernel, the CPU oracle's rate on the host cores).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+VALU_PEAK_TFLOPS = 157.3        # MI355X fp32 vector peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+METRIC = "KV-read GB/s (% of HBM peak) and attn rows/s, 16-stream decode"
+PMC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["stream_paged_attention_amd/csrc/rows_valu.hip",
+                  "stream_paged_attention_amd/csrc/device.hpp"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kv_bytes(w) -> int:
+    """Algorithmic bytes: each visible key's K and V once, all kv heads."""
+    return sum(s.key_count for s in w.segments) * w.n_kv_heads * w.head_dim * 2 * 2
+
+
+def attn_flops(w) -> int:
+    """QK^T and P.V multiply-adds (2 flops each) over every row's visible keys."""
+    total = 0
+    for s in w.segments:
+        vis = sum(s.key_count - s.n_rows + r + 1 for r in range(s.n_rows))
+        total += vis * w.n_q_heads * w.head_dim * 2 * 2
+    return total
+
+
+def traffic_entry(config: int):
+    """HBM bytes per rows launch from the committed rocprofv3 counter runs, or None
+    when the kernel source changed since they were taken."""
+    try:
+        with open(PMC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = data.get(f"config{config}")
+    if not e or e.get("kernel_hash") != kernel_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    from oracle import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    rows = None
+    if w.name == "config4":        # bounded sample: a few rows of the prompt chunk
+        rows = [0, 128, 256, 384, 511]
+    reps, used = 0, threads
+    t0 = time.perf_counter()
+    while True:
+        _, used = oracle.attn_workload(w, rows=rows, threads=threads, return_threads=True)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    if rows is None:
+        nbytes, nrows = kv_bytes(w), w.total_rows
+        sample = f"whole workload x{reps} ({el:.1f} s)"
+    else:
+        seg = w.segments[0]
+        nbytes = sum(seg.key_count - seg.n_rows + r + 1 for r in rows) * w.n_kv_heads * w.head_dim * 4
+        nrows = len(rows)
+        sample = f"{len(rows)} of {w.total_rows} rows x{reps} ({el:.1f} s)"
+    return {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": int(used),
+            "kind": "oracle", "sample": sample,
+            "rows_per_s": round(nrows * reps / el, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--copies", type=int, default=0, help="K/V copies rotated (0 = auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="time only tf_attn_rows launches (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by stream or kv head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from stream_paged_attention_amd import binding, launch, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    binding.load()
+    dev = torch.device("cuda:0")
+    w = synth.make_config(args.config)
+    pool_bytes = (w.pool_k.nbytes * 2 if w.pool_k is not None
+                  else sum(x.nbytes for x in w.store_k) * 2)
+    copies = args.copies or max(1, min(8, -(-(2 * 256 * 2 ** 20) // max(1, kv_bytes(w)))))
+    dw = launch.DeviceWorkload(w, dev, copies=copies)
+    stream = torch.cuda.current_stream(dev)
+    st = stream.cuda_stream
+    argl = [dw.args(c) for c in range(copies)]
+    logits = ids = flags = ws = None
+    if w.logits is not None and not args.kernel_only:
+        logits = launch._dev(w.logits, dev)
+        nrows, vocab = w.logits.shape
+        ids = torch.empty(nrows, dtype=torch.int32, device=dev)
+        flags = torch.empty(nrows, dtype=torch.uint8, device=dev)
+        wsb = binding.tf_argmax_workspace_bytes(nrows, vocab)
+        ws = torch.empty(wsb // 8 + 1, dtype=torch.int64, device=dev)
+    split = dw.split_keys > 0
+
+    def step(i, ev=None):
+        a = argl[i % copies]
+        if ev is not None:
+            ev[0].record(stream)
+        rc = binding.tf_attn_rows(a, st)
+        if ev is not None:
+            ev[1].record(stream)
+        if split and not args.kernel_only:
+            rc |= binding.tf_attn_merge(a, st)
+        if logits is not None:
+            rc |= binding.tf_argmax(logits.data_ptr(), nrows, vocab, vocab, ids.data_ptr(),
+                                    flags.data_ptr(), ws.data_ptr(), wsb, st)
+        return rc
+
+    for i in range(args.warmup):
+        assert step(i) == 0
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    rows_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    rows_avg_ms = sum(rows_ms) / len(rows_ms)
+    assert dw.error_word() == 0
+
+    kvb = kv_bytes(w)
+    flops = attn_flops(w)
+    value = kvb / (ms_step * 1e-3) / 1e9
+    achieved_hbm = kvb / (rows_avg_ms * 1e-3) / 1e9
+    if args.config == 2 or args.config == 1:
+        bound, ach, peak, unit = "hbm", achieved_hbm, HBM_PEAK_GBPS, "GB/s"
+    else:
+        bound, ach, peak, unit = "alu", flops / (rows_avg_ms * 1e-3) / 1e12, VALU_PEAK_TFLOPS, "TFLOP/s"
+    traffic = traffic_entry(args.config)
+    out = {
+        "metric": METRIC if args.config == 2 else
+        f"KV-read GB/s and attn rows/s, synthetic workload {args.config}",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": synth.CONFIG_TITLES[args.config],
+            "streams": len(w.segments), "rows": w.total_rows, "q_heads": w.n_q_heads,
+            "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
+            "split_keys": dw.split_keys, "kv_bytes_per_step": kvb, "attn_flops_per_step": flops,
+            "accumulate": "fp32", "kv_copies_rotated": copies, "pool_bytes_per_copy": pool_bytes,
+            "rows_per_s": round(w.total_rows / (ms_step * 1e-3), 1),
+            "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+            "rows_kernel_us": {"mean": round(rows_avg_ms * 1e3, 3),
+                               "p10": round(rows_ms[len(rows_ms) // 10] * 1e3, 3),
+                               "p50": round(rows_ms[len(rows_ms) // 2] * 1e3, 3),
+                               "p90": round(rows_ms[(9 * len(rows_ms)) // 10] * 1e3, 3)},
+            "wall_s": round(wall, 3),
+            "kernel_hash": kernel_hash(),
+        },
+        "roofline": {"bound": bound, "achieved": round(ach, 3), "peak": peak, "unit": unit,
+                     "frac": round(ach / peak, 4), "traffic": traffic,
+                     "kernel": "tf_attn_rows (rows_valu_kernel)",
+                     "hbm_gbps_rows_kernel": round(achieved_hbm, 2)},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

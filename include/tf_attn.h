@@ -1,0 +1,212 @@
+/*
+ * tf_attn.h -- C ABI of the shared-round attention library (MI355X, gfx950).
+ *
+ * One launch serves the query rows of many concurrent streams.  A segment
+ * table in device memory names, for each stream, where its K/V cache lives,
+ * which packed query rows are its own and how many keys it has; the stream's
+ * K/V sits in pages of a shared pool, in a wrapping ring, or in one
+ * contiguous buffer.  tf_attn_rows writes split-K partials (or the output
+ * directly when there is one split), tf_attn_merge combines the partials with
+ * an online-softmax merge, and tf_argmax picks each row's first largest
+ * logit and flags rows that hold a nonfinite one.
+ *
+ * Sources (the pages this library is built from):
+ *  - TensorFold PR #1503, "lfm2_moe CUDA: attention pages from the shared KV
+ *    pool, and the prompt cache": the segment table of cache addresses, row
+ *    offsets and key counts that lets one launch per layer serve every stream
+ *    (the shared-rounds commit); reads through a slot's page table and the
+ *    refusal of rows past a slot's pages (the pool-leasing commit); the GPU
+ *    argmax with its tie and nonfinite rules (the lfm2_argmax commit).
+ *  - TensorFold PR #1653, "spark25 CUDA: the full layers' caches in pages of
+ *    the core pool ...": paged decode part/merge kernels, prompt rows read
+ *    through the slot's page-table row in pages of whole 32-key tiles, the
+ *    page lookup hoisted out of the key loop.
+ *  - TensorFold PR #1562, "Qwen3.6 MTP drafter on CUDA: draft a shared
+ *    round's streams together": the rows kernel that reads each row's ring,
+ *    slots and segment from a table and must equal one launch per segment;
+ *    ring slots folded in groups with the next group in flight.
+ *
+ * Conventions
+ *  - All tensors are bf16 (stored as 16-bit patterns), accumulation is fp32,
+ *    outputs are rounded to bf16 with round-to-nearest-even.
+ *  - Ownership: the caller allocates every buffer (device memory unless
+ *    marked "host").  The library allocates nothing, keeps no state between
+ *    calls, never synchronises the stream and launches only on the stream it
+ *    is given.  Calls are thread-safe.
+ *  - Errors: scalar arguments are checked on the host before anything is
+ *    launched; a bad call returns a negative TF_E_* code and launches
+ *    nothing.  Segment contents live in device memory and are checked by the
+ *    kernels: an invalid segment sets bits in the optional device error word
+ *    (TF_ERR_*), and its rows are written as NaN when its row range and
+ *    partial range are themselves valid (otherwise nothing is written for
+ *    it).  tf_check_segments runs the same checks on a host copy.
+ *  - NaN rule: keys outside a row's visible range are never used.  If any
+ *    visible score of a (row, head) is NaN or +-Inf, every output element of
+ *    that (row, head) is NaN.  Otherwise an output element whose value is not
+ *    finite is written as NaN (0x7FC0).
+ */
+#ifndef TF_ATTN_H
+#define TF_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* How a segment's K/V is stored (one kind per launch). */
+typedef enum tf_kv_kind {
+    TF_KV_CONTIG = 0, /* per stream: k, v -> [n_kv_heads][capacity][head_dim]               */
+    TF_KV_PAGED = 1,  /* shared pool: k, v -> [pool_pages][n_kv_heads][page_size][head_dim]; */
+                      /* logical key j is row j % page_size of pool page pages[j / page_size] */
+    TF_KV_RING = 2    /* per stream: k, v -> [n_kv_heads][capacity][head_dim], capacity = ring */
+                      /* slots; logical key j is in slot (first + j) mod capacity            */
+} tf_kv_kind;
+
+/* Return codes. */
+enum {
+    TF_OK = 0,
+    TF_E_INVALID = -1,     /* null pointer, negative count, n_q_heads % n_kv_heads != 0, ...     */
+    TF_E_UNSUPPORTED = -2, /* head_dim not 64/128/256, page_size not a power of two in
+                              [32, 1024], split_keys not a multiple of 32                        */
+    TF_E_PAST_PAGES = -3,  /* a segment holds more keys than its pages / ring / buffer (host check) */
+    TF_E_WORKSPACE = -4,   /* partials or argmax workspace missing or too small                  */
+    TF_E_LAUNCH = -5       /* the HIP runtime refused the launch                                 */
+};
+
+/* Bits the kernels OR into the optional device error word. */
+enum {
+    TF_ERR_PAST_PAGES = 1, /* key_count > capacity (x page_size for PAGED)                       */
+    TF_ERR_BAD_PAGE = 2,   /* a page id outside [0, pool_pages)                                  */
+    TF_ERR_BAD_ROWS = 4,   /* n_rows < 1, n_rows > key_count, or rows outside [0, total_rows)    */
+    TF_ERR_BAD_RING = 8,   /* ring first outside [0, capacity)                                   */
+    TF_ERR_PARTIALS = 16   /* the segment's partial records fall outside the workspace           */
+};
+
+/*
+ * One stream's span of a shared launch.  The table (an array of these)
+ * lives in device memory.  48 bytes, 8-byte aligned.
+ *
+ * Row r (0-based) of an n-row segment is packed query row row_offset + r; it
+ * sees logical keys [0, key_count - n_rows + r + 1): the segment's new rows
+ * are its newest keys and each row sees itself (causal count).
+ */
+typedef struct tf_segment {
+    const void *k;          /* bf16 K storage (see tf_kv_kind)                                 */
+    const void *v;          /* bf16 V storage, same layout as k                                */
+    const int32_t *pages;   /* PAGED: logical page -> pool page id; NULL otherwise             */
+    int32_t capacity;       /* PAGED: entries of pages[]; RING: slots; CONTIG: keys allocated  */
+    int32_t first;          /* RING: slot that holds logical key 0; 0 otherwise                */
+    int32_t row_offset;     /* first packed query row of this segment                          */
+    int32_t n_rows;         /* 1 <= n_rows <= key_count                                        */
+    int32_t key_count;      /* keys visible to the segment's last row                          */
+    int32_t partial_offset; /* first partial record of this segment (see tf_plan_partials)     */
+} tf_segment;
+
+/*
+ * Arguments of tf_attn_rows / tf_attn_merge.  Host memory; the pointers in
+ * it are device pointers.
+ *
+ * Partial records: record index
+ *     partial_offset + (r * n_q_heads + h) * n_splits + t,
+ * with n_splits = ceil(key_count / split_keys) of the record's segment,
+ * holds split t (keys [t * split_keys, (t + 1) * split_keys) of row r's
+ * visible keys) of row r, query head h.  A record is head_dim + 4 floats:
+ *     [0] m  : max of the split's scaled scores (natural-log units), -inf if
+ *              the split is empty, NaN if it saw a nonfinite score;
+ *     [1] l  : sum over the split of exp(score - m);
+ *     [2..3] : unused;
+ *     [4..]  : o[head_dim] = sum over the split of exp(score - m) * v.
+ */
+typedef struct tf_attn_args {
+    int32_t kind;             /* tf_kv_kind                                                  */
+    int32_t n_segments;       /* >= 0                                                        */
+    int32_t total_rows;       /* packed query rows of q and out                              */
+    int32_t max_rows;         /* >= every segment's n_rows (grid sizing only)                */
+    int32_t max_keys;         /* >= every segment's key_count (grid sizing only)             */
+    int32_t n_q_heads;        /* Hq                                                          */
+    int32_t n_kv_heads;       /* Hkv; query head h reads kv head h / (Hq / Hkv)              */
+    int32_t head_dim;         /* 64, 128 or 256                                              */
+    int32_t page_size;        /* PAGED: keys per page (power of two, 32..1024); else ignored */
+    int32_t pool_pages;       /* PAGED: pages in the pool (page ids are checked against it)  */
+    int32_t split_keys;       /* keys per partial (multiple of 32), or 0 = one split: then
+                                 tf_attn_rows writes out directly and needs no partials      */
+    float scale;              /* score = scale * (q . k), normally 1 / sqrt(head_dim)        */
+    const tf_segment *segs;   /* device: n_segments entries                                  */
+    const void *q;            /* device bf16 [total_rows][n_q_heads][head_dim]               */
+    void *out;                /* device bf16 [total_rows][n_q_heads][head_dim]               */
+    float *partials;          /* device fp32 records (split_keys > 0)                        */
+    size_t partials_bytes;    /* size of partials                                            */
+    int32_t *err;             /* device int32 error word (TF_ERR_* bits ORed in), or NULL    */
+} tf_attn_args;
+
+/*
+ * tf_attn_rows: attention of every segment's rows over its own keys.
+ * With split_keys > 0 writes one partial record per (row, head, split) of
+ * every segment; with split_keys == 0 writes out.  Each (row, head)'s
+ * result depends only on its own segment: a batched launch is bit-equal to
+ * one launch per segment, and to the same keys stored as pages, a ring or a
+ * contiguous buffer.  Returns TF_OK or a TF_E_* code (nothing launched).
+ */
+int tf_attn_rows(const tf_attn_args *a, hipStream_t stream);
+
+/*
+ * tf_attn_merge: combine each (row, head)'s partial records into out:
+ *     M = max m_t, L = sum l_t e^(m_t - M), out = sum o_t e^(m_t - M) / L,
+ * splits taken in order t = 0, 1, ...; a NaN record makes the output NaN.
+ * Needs split_keys > 0 and the partials tf_attn_rows wrote with the same
+ * arguments (TensorFold PR #1653: the paged decode merge, with nonfinite
+ * heads kept off the fast path).
+ */
+int tf_attn_merge(const tf_attn_args *a, hipStream_t stream);
+
+/*
+ * tf_argmax: for each row of bf16 logits (row i starts at logits + i *
+ * row_stride elements; the first `vocab` are read) writes ids[i], the lowest
+ * id among the largest values, and flags[i] = 1 if any of the row's logits is
+ * NaN or +-Inf (else 0).  NaN ranks as -inf for the id, +0.0 equals -0.0
+ * (TensorFold PR #1503, the lfm2_argmax commit and the router note).
+ * workspace: device memory of at least tf_argmax_workspace_bytes(n_rows,
+ * vocab) bytes, contents ignored on entry.  Returns TF_E_INVALID for null
+ * pointers, vocab < 1, row_stride < vocab; TF_E_WORKSPACE if the workspace is
+ * too small.
+ */
+int tf_argmax(const void *logits, int32_t n_rows, int32_t vocab, int64_t row_stride,
+              int32_t *ids, uint8_t *flags, void *workspace, size_t workspace_bytes,
+              hipStream_t stream);
+
+/* Workspace bytes tf_argmax needs for n_rows rows of vocab logits. */
+size_t tf_argmax_workspace_bytes(int32_t n_rows, int32_t vocab);
+
+/*
+ * tf_plan_partials (host): assign each segment's partial_offset in the
+ * host table (segments laid out in order) and return the workspace size in
+ * bytes for split_keys > 0.  Reads n_rows and key_count of each host
+ * segment.  Returns TF_E_INVALID on bad counts, TF_E_UNSUPPORTED on a bad
+ * split_keys or head_dim.
+ */
+int tf_plan_partials(tf_segment *host_segs, int32_t n_segments, int32_t n_q_heads,
+                     int32_t head_dim, int32_t split_keys, size_t *partials_bytes);
+
+/*
+ * tf_check_segments (host): the kernels' per-segment checks on a host copy
+ * of the table, plus the ones only the host can do (rows of different
+ * segments must not overlap; max_rows / max_keys must bound the table; the
+ * pages pointer of a PAGED segment must be non-null).  Returns TF_OK,
+ * TF_E_PAST_PAGES (a segment holds more keys than its storage),
+ * TF_E_WORKSPACE (partial records outside the workspace) or TF_E_INVALID.
+ * Page ids live in device memory and are checked by the kernels only.
+ */
+int tf_check_segments(const tf_attn_args *a, const tf_segment *host_segs);
+
+/* Static description of a return code. */
+const char *tf_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TF_ATTN_H */

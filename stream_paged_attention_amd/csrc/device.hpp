@@ -1,0 +1,102 @@
+// Device-side helpers shared by the HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tf_attn.h"
+
+namespace tfa {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr uint16_t kBf16NaN = 0x7FC0;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Parameters of one rows launch (passed by value to the kernels).
+struct RowsParams {
+    const tf_segment *segs;
+    const uint16_t *q;
+    uint16_t *out;
+    float *partials;
+    int64_t max_records;   // records the partials workspace holds
+    int32_t *err;
+    int n_segments;
+    int total_rows;
+    int hq;
+    int hkv;
+    int group;             // hq / hkv
+    int page_size;
+    int page_shift;        // log2(page_size)
+    int pool_pages;
+    int split_keys;        // 0 = one split per (row, head), written straight to out
+    int n_split_max;       // grid extent per segment
+    float c_log2;          // scale * log2(e): scores are kept in base-2 units
+};
+
+// v_dot2_f32_bf16: a.x*b.x + a.y*b.y + c with fp32 accumulation.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Exact widening of the low / high bf16 of a packed pair.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN -> canonical NaN.
+__device__ __forceinline__ uint16_t bf16_rne(float x)
+{
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return kBf16NaN;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Output rule: a nonfinite value is written as NaN.
+__device__ __forceinline__ uint16_t bf16_out(float x)
+{
+    return __builtin_isfinite(x) ? bf16_rne(x) : kBf16NaN;
+}
+
+// v_exp_f32 (2^x).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP lane permutation inside a 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row receives it.
+// quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror, row_mirror.
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    x += dpp<0x140>(x);
+    return x;
+}
+
+// Online-softmax state merge (base-2 units): (m, l, o) <- (m, l, o) (+) (mb, lb, ob).
+// An empty state is (-inf, 0, 0); two empties stay empty.
+__device__ __forceinline__ void merge_scales(float m, float mb, float &mn, float &fa, float &fb)
+{
+    mn = fmaxf(m, mb);
+    const float ms = (mn == -INFINITY) ? 0.0f : mn;
+    fa = exp2_fast(m - ms);
+    fb = exp2_fast(mb - ms);
+}
+
+__device__ __forceinline__ void report(int32_t *err, int bits)
+{
+    if (err != nullptr && bits != 0)
+        atomicOr(err, bits);
+}
+
+}  // namespace tfa

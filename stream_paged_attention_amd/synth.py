@@ -120,36 +120,36 @@ class Workload:
 # ----------------------------------------------------------------------------
 
 def place_paged(k_logical: Sequence[np.ndarray], page_size: int, pool_pages: int,
-                page_lists: Sequence[np.ndarray]) -> np.ndarray:
+                page_lists: Sequence[np.ndarray], fill=BF16_NAN) -> np.ndarray:
     """Scatter each stream's logical rows into the pool pages its list names."""
     assert len(k_logical) == len(page_lists)
     hkv, d = k_logical[0].shape[1], k_logical[0].shape[2]
-    pool = np.full((pool_pages, hkv, page_size, d), BF16_NAN, dtype=np.uint16)
+    pool = np.full((pool_pages, hkv, page_size, d), fill, dtype=np.uint16)
     for kl, pages in zip(k_logical, page_lists):
         kc = kl.shape[0]
         npg = -(-kc // page_size)
         assert len(pages) >= npg
-        padded = np.full((npg * page_size, hkv, d), BF16_NAN, dtype=np.uint16)
+        padded = np.full((npg * page_size, hkv, d), fill, dtype=np.uint16)
         padded[:kc] = kl
         blocks = padded.reshape(npg, page_size, hkv, d).transpose(0, 2, 1, 3)
         pool[np.asarray(pages[:npg], dtype=np.int64)] = blocks
     return pool
 
 
-def place_ring(kl: np.ndarray, slots: int, first: int) -> np.ndarray:
+def place_ring(kl: np.ndarray, slots: int, first: int, fill=BF16_NAN) -> np.ndarray:
     """Put logical key j of one stream into ring slot (first + j) mod slots."""
     kc, hkv, d = kl.shape
     assert kc <= slots and 0 <= first < slots
-    ring = np.full((hkv, slots, d), BF16_NAN, dtype=np.uint16)
+    ring = np.full((hkv, slots, d), fill, dtype=np.uint16)
     idx = (first + np.arange(kc, dtype=np.int64)) % slots
     ring[:, idx, :] = kl.transpose(1, 0, 2)
     return ring
 
 
-def place_contig(kl: np.ndarray, capacity: int) -> np.ndarray:
+def place_contig(kl: np.ndarray, capacity: int, fill=BF16_NAN) -> np.ndarray:
     kc, hkv, d = kl.shape
     assert kc <= capacity
-    buf = np.full((hkv, capacity, d), BF16_NAN, dtype=np.uint16)
+    buf = np.full((hkv, capacity, d), fill, dtype=np.uint16)
     buf[:, :kc, :] = kl.transpose(1, 0, 2)
     return buf
 
@@ -177,7 +177,7 @@ def _segments(n_rows: Sequence[int], key_counts: Sequence[int]) -> List[Segment]
 def restore(w: Workload, kind: str, *, seed: int = 0, pool_pages: Optional[int] = None,
             page_size: Optional[int] = None, ring_slots: Optional[int] = None,
             ring_first: Optional[Sequence[int]] = None,
-            capacity: Optional[Sequence[int]] = None) -> Workload:
+            capacity: Optional[Sequence[int]] = None, fill=BF16_NAN) -> Workload:
     """Same logical K/V and Q, placed into another storage kind or permutation.
 
     Used for the equality checks (two page permutations, paged against
@@ -197,23 +197,23 @@ def restore(w: Workload, kind: str, *, seed: int = 0, pool_pages: Optional[int] 
         for s, pl in zip(segs, lists):
             s.pages, s.capacity = pl, len(pl)
         out.page_size = p
-        out.pool_k = place_paged(w.k_logical, p, npool, lists)
-        out.pool_v = place_paged(w.v_logical, p, npool, lists)
+        out.pool_k = place_paged(w.k_logical, p, npool, lists, fill)
+        out.pool_v = place_paged(w.v_logical, p, npool, lists, fill)
     elif kind == KIND_RING:
         out.store_k, out.store_v = [], []
         for i, s in enumerate(segs):
             slots = ring_slots or s.key_count
             first = int(ring_first[i]) if ring_first is not None else int(rng.integers(0, slots))
             s.capacity, s.first = slots, first
-            out.store_k.append(place_ring(w.k_logical[i], slots, first))
-            out.store_v.append(place_ring(w.v_logical[i], slots, first))
+            out.store_k.append(place_ring(w.k_logical[i], slots, first, fill))
+            out.store_v.append(place_ring(w.v_logical[i], slots, first, fill))
     elif kind == KIND_CONTIG:
         out.store_k, out.store_v = [], []
         for i, s in enumerate(segs):
             cap = int(capacity[i]) if capacity is not None else s.key_count
             s.capacity = cap
-            out.store_k.append(place_contig(w.k_logical[i], cap))
-            out.store_v.append(place_contig(w.v_logical[i], cap))
+            out.store_k.append(place_contig(w.k_logical[i], cap, fill))
+            out.store_v.append(place_contig(w.v_logical[i], cap, fill))
     else:
         raise ValueError(kind)
     return out

@@ -1,0 +1,326 @@
+"""GPU parity of the HIP path against the float64 oracle, and its equalities.
+
+Tolerance (spec contract): |bf16 output - float64 oracle| <= 2e-3 for the
+five synthetic workloads, NaN positions identical; argmax ids and flags
+bit-exact.  Small hand-shaped cases can produce outputs of magnitude >= 0.5,
+where bf16's own half-ulp (2^-9 |x|) exceeds 2e-3; there the bound is
+2e-3 + 2^-8 |oracle| (the rounding of the stored result plus the fp32 path).
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import oracle
+from stream_paged_attention_amd import binding, launch, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def f32(bits):
+    return synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def assert_close(got_bits, ref, tol=2e-3, rel=0.0, what=""):
+    got = f32(got_bits)
+    assert got.shape == ref.shape
+    nan_g, nan_r = np.isnan(got), np.isnan(ref)
+    assert np.array_equal(nan_g, nan_r), f"{what}: NaN positions differ ({nan_g.sum()} vs {nan_r.sum()})"
+    fin = ~nan_r
+    err = np.abs(got[fin] - ref[fin])
+    bound = tol + rel * np.abs(ref[fin])
+    worst = float(np.max(err - bound)) if err.size else -1.0
+    assert worst <= 0.0, f"{what}: max |err| {float(err.max()):.3e} exceeds the bound"
+    return float(err.max()) if err.size else 0.0
+
+
+REL_SMALL = 2.0 ** -8
+
+
+@pytest.fixture(scope="module")
+def configs(gpu):
+    cache = {}
+
+    def get(n):
+        if n not in cache:
+            w = synth.make_config(n)
+            cache[n] = (w, launch.DeviceWorkload(w, gpu))
+        return cache[n]
+    return get
+
+
+# --------------------------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5])
+def test_config_matches_oracle(configs, n):
+    w, dw = configs(n)
+    print(f"config {n}: {synth.CONFIG_TITLES[n]}", flush=True)
+    assert dw.check_table() == binding.TF_OK
+    dw.run()
+    got = dw.output()
+    ref = oracle.attn_workload(w)
+    err = assert_close(got, ref, what=f"config {n}")
+    assert dw.error_word() == 0
+    print(f"config {n}: max |err| = {err:.3e}")
+
+
+def test_config4_sampled_rows_match_oracle(configs):
+    w, dw = configs(4)
+    dw.run()
+    got = dw.output()
+    rng = np.random.Generator(np.random.PCG64(44))
+    rows = sorted(set([0, 1, 31, 32, 255, 256, 510, 511] + rng.choice(512, 16, replace=False).tolist()))
+    ref = oracle.attn_workload(w, rows=rows)
+    err = assert_close(got[rows], ref, what="config 4 sampled rows")
+    assert dw.error_word() == 0
+    print(f"config 4: {len(rows)} sampled rows, max |err| = {err:.3e}")
+
+
+@pytest.mark.parametrize("n", [1, 3, 5])
+def test_config_argmax_bit_exact(configs, n):
+    w, _ = configs(n)
+    ids, flags = launch.argmax(w.logits)
+    rids, rflags = oracle.argmax(w.logits)
+    np.testing.assert_array_equal(ids, rids)
+    np.testing.assert_array_equal(flags, rflags)
+    if n == 5:
+        assert flags[4] == 1 and flags[5] == 1 and flags[:4].sum() == 0
+        assert ids[0] == 0
+
+
+@pytest.mark.parametrize("n", [2, 3, 5])
+def test_batched_equals_per_segment(configs, n):
+    w, dw = configs(n)
+    dw.run()
+    batched = dw.output()
+    single = dw.run_per_segment()
+    assert np.array_equal(batched, single), f"config {n}: batched launch differs from per-segment"
+
+
+def test_repeats_are_byte_identical(configs):
+    w, dw = configs(2)
+    outs = []
+    for _ in range(5):
+        dw.out.zero_()
+        dw.run()
+        outs.append(dw.output().copy())
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+# --------------------------------------------------------------------------- storage equalities
+
+def _small_paged(seed=3, d=128, hq=8, hkv=2, rows=(1, 4, 2, 16), keys=(900, 97, 33, 1500),
+                 split=64):
+    return synth.make_workload("small", synth.KIND_PAGED, hq, hkv, d, list(rows), list(keys),
+                               seed=seed, page_size=32, pool_pages=200, split_keys=split)
+
+
+def test_page_permutations_are_byte_equal(gpu):
+    w = _small_paged()
+    a = launch.DeviceWorkload(w, gpu)
+    a.run()
+    b = launch.DeviceWorkload(synth.restore(w, synth.KIND_PAGED, seed=1234, pool_pages=300), gpu)
+    b.run()
+    assert np.array_equal(a.output(), b.output())
+
+
+def test_paged_contig_ring_are_byte_equal(gpu):
+    w = _small_paged(seed=5)
+    outs = []
+    for kind, kw in ((synth.KIND_PAGED, {}), (synth.KIND_CONTIG, dict(capacity=[1000, 200, 40, 1600])),
+                     (synth.KIND_RING, dict(ring_slots=None, ring_first=[899, 50, 0, 1234]))):
+        ww = synth.restore(w, kind, seed=9, **kw)
+        dw = launch.DeviceWorkload(ww, gpu)
+        assert dw.check_table() == binding.TF_OK
+        dw.run()
+        outs.append(dw.output())
+    assert np.array_equal(outs[0], outs[1]), "paged != contiguous"
+    assert np.array_equal(outs[0], outs[2]), "wrapped ring != contiguous"
+
+
+def test_poison_outside_ranges_changes_nothing(gpu):
+    w = _small_paged(seed=6)
+    outs = []
+    for kind, kw in ((synth.KIND_PAGED, dict(pool_pages=180)), (synth.KIND_RING, dict(ring_slots=1700)),
+                     (synth.KIND_CONTIG, dict(capacity=[1024, 128, 64, 1600]))):
+        pair = []
+        for fill in (synth.BF16_NAN, np.uint16(0)):
+            dw = launch.DeviceWorkload(synth.restore(w, kind, seed=2, fill=fill, **kw), gpu)
+            dw.run()
+            pair.append(dw.output())
+        assert np.array_equal(pair[0], pair[1]), f"{kind}: NaN poison outside the range leaked"
+        outs.append(pair[0])
+    ref = oracle.attn_workload(w)
+    assert_close(outs[0], ref, rel=REL_SMALL, what="poisoned paged")
+
+
+# --------------------------------------------------------------------------- shapes, splits, edges
+
+SHAPES = [
+    # kind, D, Hq, Hkv, rows, keys, split
+    ("paged", 64, 8, 2, [1], [256], 0),
+    ("paged", 64, 4, 4, [3, 1], [70, 33], 32),
+    ("paged", 128, 32, 8, [1, 1, 1], [512, 513, 4096], 512),
+    ("paged", 128, 16, 2, [16, 2], [4200, 17], 512),
+    ("paged", 128, 8, 1, [5], [5], 32),            # every key is a new row
+    ("paged", 128, 8, 8, [1], [1], 0),             # a single key
+    ("paged", 256, 16, 4, [1, 7, 16], [2049, 300, 2064], 512),
+    ("paged", 256, 16, 4, [9], [1000], 0),
+    ("contig", 128, 16, 2, [3, 1], [777, 64], 96),
+    ("ring", 128, 16, 2, [16, 1, 4], [4200, 333, 80], 512),
+    ("ring", 256, 8, 2, [2], [129], 64),
+]
+
+
+@pytest.mark.parametrize("kind,d,hq,hkv,rows,keys,split", SHAPES)
+def test_shapes_match_oracle(gpu, kind, d, hq, hkv, rows, keys, split):
+    print(f"shape {kind} D{d} {hq}/{hkv} rows {rows} keys {keys} split {split}", flush=True)
+    kw = {}
+    if kind == "paged":
+        kw = dict(page_size=32, pool_pages=sum(-(-k // 32) for k in keys) + 7)
+    elif kind == "ring":
+        kw = dict(ring_slots=[k + 5 for k in keys], ring_heads=[(k * 7) % (k + 5) for k in keys])
+    elif kind == "contig":
+        kw = dict(contig_capacity=[k + 3 for k in keys])
+    w = synth.make_workload("shape", kind, hq, hkv, d, rows, keys, seed=sum(keys) + d,
+                            split_keys=split, **kw)
+    dw = launch.DeviceWorkload(w, gpu)
+    assert dw.check_table() == binding.TF_OK
+    dw.run()
+    assert_close(dw.output(), oracle.attn_workload(w), rel=REL_SMALL, what="shape")
+    assert dw.error_word() == 0
+
+
+@pytest.mark.parametrize("page_size", [64, 256])
+def test_other_page_sizes(gpu, page_size):
+    w = synth.make_workload("pages", synth.KIND_PAGED, 8, 2, 128, [1, 3], [1000, 257], seed=8,
+                            page_size=page_size, pool_pages=40, split_keys=256)
+    dw = launch.DeviceWorkload(w, gpu)
+    dw.run()
+    assert_close(dw.output(), oracle.attn_workload(w), rel=REL_SMALL, what=f"P{page_size}")
+
+
+def test_different_split_sizes_agree_within_tolerance(gpu):
+    w = _small_paged(seed=12)
+    ref = oracle.attn_workload(w)
+    for split in (0, 32, 128, 512):
+        dw = launch.DeviceWorkload(w, gpu, split_keys=split)
+        dw.run()
+        assert_close(dw.output(), ref, rel=REL_SMALL, what=f"split {split}")
+
+
+def test_partial_records_match_oracle_partials(gpu):
+    split = 64
+    w = synth.make_workload("parts", synth.KIND_PAGED, 8, 2, 128, [3, 1], [200, 130], seed=14,
+                            page_size=32, pool_pages=20, split_keys=split)
+    dw = launch.DeviceWorkload(w, gpu)
+    dw.run()
+    recs = dw.partial_records()
+    m, l, o = oracle.attn_partials([s.n_rows for s in w.segments], [s.key_count for s in w.segments],
+                                   w.q, w.k_logical, w.v_logical, n_q_heads=8, n_kv_heads=2,
+                                   head_dim=128, scale=w.scale, split=split)
+    row = 0
+    for seg in w.segments:
+        ns = -(-seg.key_count // split)
+        for r in range(seg.n_rows):
+            for h in range(8):
+                for t in range(ns):
+                    rec = recs[dw.host_segs[w.segments.index(seg)].partial_offset + (r * 8 + h) * ns + t]
+                    mr, lr, orr = m[row, h, t], l[row, h, t], o[row, h, t]
+                    if mr == -np.inf:
+                        assert rec[0] == -np.inf and rec[1] == 0 and not np.any(rec[4:])
+                        continue
+                    assert abs(rec[0] - mr) <= 1e-5 * max(1.0, abs(mr))
+                    assert abs(rec[1] - lr) <= 1e-5 * lr
+                    assert np.max(np.abs(rec[4:] - orr)) <= 1e-5 * lr * 4
+            row += 1
+
+
+# --------------------------------------------------------------------------- NaN rule
+
+def _nan_case(gpu, plant):
+    w = synth.make_workload("nan", synth.KIND_PAGED, 8, 2, 128, [4, 1], [300, 70], seed=21,
+                            page_size=32, pool_pages=20, split_keys=64)
+    plant(w)
+    w2 = synth.restore(w, synth.KIND_PAGED, seed=3)
+    dw = launch.DeviceWorkload(w2, gpu)
+    dw.run()
+    got, ref = dw.output(), oracle.attn_workload(w2)
+    assert_close(got, ref, rel=REL_SMALL, what="nan rule")
+    return f32(got)
+
+
+def test_nan_key_poisons_its_group(gpu):
+    def plant(w):
+        w.k_logical[0][100, 1, 5] = synth.BF16_NAN
+    got = _nan_case(gpu, plant)
+    assert np.isnan(got[0:4, 4:8]).all() and np.isfinite(got[0:4, 0:4]).all()
+
+
+def test_nan_value_poisons_one_lane(gpu):
+    def plant(w):
+        w.v_logical[0][10, 0, 77] = synth.BF16_POS_INF
+    got = _nan_case(gpu, plant)
+    assert np.isnan(got[0:4, 0:4, 77]).all()
+    assert np.isfinite(got[0:4, 0:4, :77]).all()
+
+
+def test_nan_in_newest_key_reaches_only_last_row(gpu):
+    def plant(w):
+        w.k_logical[0][299, :, 3] = synth.BF16_NAN
+        w.v_logical[0][299, :, :] = synth.BF16_NAN
+    got = _nan_case(gpu, plant)
+    assert np.isnan(got[3]).all() and np.isfinite(got[0:3]).all() and np.isfinite(got[4]).all()
+
+
+# --------------------------------------------------------------------------- device error word
+
+def test_bad_page_id_sets_error_and_nan(gpu):
+    w = _small_paged(seed=30)
+    dw = launch.DeviceWorkload(w, gpu)
+    pages = dw.pages.cpu().numpy()
+    pages[int(dw.page_off[1]) + 1] = 10 ** 6          # segment 1, second page
+    dw.pages.copy_(__import__("torch").from_numpy(pages).to(dw.pages.device))
+    dw.run()
+    got = f32(dw.output())
+    assert dw.error_word() & binding.TF_ERR_BAD_PAGE
+    s1 = w.segments[1]
+    assert np.isnan(got[s1.row_offset:s1.row_offset + s1.n_rows]).all()
+    s0 = w.segments[0]
+    assert np.isfinite(got[s0.row_offset:s0.row_offset + s0.n_rows]).all()
+
+
+def test_key_count_past_pages_sets_error(gpu):
+    import ctypes
+    import torch
+    w = _small_paged(seed=31)
+    dw = launch.DeviceWorkload(w, gpu)
+    hs = dw._host_segments(0)
+    for i in range(len(hs)):
+        hs[i].partial_offset = dw.host_segs[i].partial_offset
+    hs[2].capacity = 1                                   # 33 keys in one page of 32
+    dw.tables[0] = dw._upload(hs)
+    assert binding.tf_check_segments(dw.args(0), hs) == binding.TF_E_PAST_PAGES
+    dw.run()
+    got = f32(dw.output())
+    assert dw.error_word() & binding.TF_ERR_PAST_PAGES
+    s2 = w.segments[2]
+    assert np.isnan(got[s2.row_offset:s2.row_offset + s2.n_rows]).all()
+    assert np.isfinite(got[:s2.row_offset]).all()
+
+
+def test_argmax_small_cases(gpu):
+    from tests import pins
+    x = pins.argmax_rows(seed=40, rows=12, vocab=9000)
+    ids, flags = launch.argmax(x)
+    rids, rflags = oracle.argmax(x)
+    np.testing.assert_array_equal(ids, rids)
+    np.testing.assert_array_equal(flags, rflags)
+    # a row stride wider than the vocabulary, with a larger value past the end
+    wide = np.full((12, 9008), synth.f32_to_bf16_bits(np.float32(50.0)), dtype=np.uint16)
+    wide[:, :9001] = np.concatenate([x, x[:, :1]], axis=1)
+    ids2, flags2 = launch.argmax(wide, vocab=9001)
+    rids2, rflags2 = oracle.argmax(wide, vocab=9001)
+    np.testing.assert_array_equal(ids2, rids2)
+    np.testing.assert_array_equal(flags2, rflags2)
