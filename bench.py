@@ -15,7 +15,6 @@ step, roofline of the rows kernel, the CPU oracle's rate on the host cores).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,16 +29,6 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 METRIC = "KV-read GB/s (% of HBM peak) and attn rows/s, 16-stream decode"
 PMC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["stream_paged_attention_amd/csrc/rows_valu.hip",
-                  "stream_paged_attention_amd/csrc/device.hpp"]
-
-
-def kernel_hash() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def kv_bytes(w) -> int:
@@ -64,6 +53,7 @@ def traffic_entry(config: int):
             data = json.load(f)
     except (OSError, ValueError):
         return None
+    from stream_paged_attention_amd.profsum import kernel_hash
     e = data.get(f"config{config}")
     if not e or e.get("kernel_hash") != kernel_hash():
         return None
@@ -108,6 +98,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kernel-only", action="store_true",
                     help="time only tf_attn_rows launches (for profiler runs)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run 20 plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -121,8 +113,16 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
-    binding.load()
     dev = torch.device("cuda:0")
+    if args.copy_mib:
+        x = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(20):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": x.numel(), "copies": 20}), flush=True)
+        return 0
+    binding.load()
     w = synth.make_config(args.config)
     pool_bytes = (w.pool_k.nbytes * 2 if w.pool_k is not None
                   else sum(x.nbytes for x in w.store_k) * 2)
@@ -141,13 +141,9 @@ def main() -> int:
         ws = torch.empty(wsb // 8 + 1, dtype=torch.int64, device=dev)
     split = dw.split_keys > 0
 
-    def step(i, ev=None):
+    def step(i):
         a = argl[i % copies]
-        if ev is not None:
-            ev[0].record(stream)
         rc = binding.tf_attn_rows(a, st)
-        if ev is not None:
-            ev[1].record(stream)
         if split and not args.kernel_only:
             rc |= binding.tf_attn_merge(a, st)
         if logits is not None:
@@ -158,24 +154,29 @@ def main() -> int:
     for i in range(args.warmup):
         assert step(i) == 0
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
-    rows_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    rows_avg_ms = sum(rows_ms) / len(rows_ms)
+    # the rows kernel alone: the same launches back to back between one event
+    # pair on the launch stream (average launch duration, gaps included)
+    n_rows_runs = min(args.steps, 1000)
+    start.record(stream)
+    for i in range(n_rows_runs):
+        binding.tf_attn_rows(argl[i % copies], st)
+    end.record(stream)
+    torch.cuda.synchronize()
+    rows_avg_ms = start.elapsed_time(end) / n_rows_runs
     assert dw.error_word() == 0
 
+    from stream_paged_attention_amd.profsum import kernel_hash as kernel_hash_now
     kvb = kv_bytes(w)
     flops = attn_flops(w)
     value = kvb / (ms_step * 1e-3) / 1e9
@@ -207,12 +208,9 @@ def main() -> int:
             "accumulate": "fp32", "kv_copies_rotated": copies, "pool_bytes_per_copy": pool_bytes,
             "rows_per_s": round(w.total_rows / (ms_step * 1e-3), 1),
             "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
-            "rows_kernel_us": {"mean": round(rows_avg_ms * 1e3, 3),
-                               "p10": round(rows_ms[len(rows_ms) // 10] * 1e3, 3),
-                               "p50": round(rows_ms[len(rows_ms) // 2] * 1e3, 3),
-                               "p90": round(rows_ms[(9 * len(rows_ms)) // 10] * 1e3, 3)},
+            "rows_kernel_us": round(rows_avg_ms * 1e3, 3),
             "wall_s": round(wall, 3),
-            "kernel_hash": kernel_hash(),
+            "kernel_hash": kernel_hash_now(),
         },
         "roofline": {"bound": bound, "achieved": round(ach, 3), "peak": peak, "unit": unit,
                      "frac": round(ach / peak, 4), "traffic": traffic,

@@ -115,11 +115,15 @@ typedef struct tf_segment {
  * with n_splits = ceil(key_count / split_keys) of the record's segment,
  * holds split t (keys [t * split_keys, (t + 1) * split_keys) of row r's
  * visible keys) of row r, query head h.  A record is head_dim + 4 floats:
- *     [0] m  : max of the split's scaled scores (natural-log units), -inf if
- *              the split is empty, NaN if it saw a nonfinite score;
+ *     [0] m  : reference for the split's scaled scores (natural-log units):
+ *              one of them, at most 8 ln 2 below their max (so no weight
+ *              exceeds 2^8); -inf if the split is empty, NaN if it saw a
+ *              nonfinite score;
  *     [1] l  : sum over the split of exp(score - m);
  *     [2..3] : unused;
  *     [4..]  : o[head_dim] = sum over the split of exp(score - m) * v.
+ * Any m gives the same softmax: m + ln(l) (the split's log-sum-exp) and o / l
+ * are what a record fixes.
  */
 typedef struct tf_attn_args {
     int32_t kind;             /* tf_kv_kind                                                  */
@@ -156,7 +160,8 @@ int tf_attn_rows(const tf_attn_args *a, hipStream_t stream);
 /*
  * tf_attn_merge: combine each (row, head)'s partial records into out:
  *     M = max m_t, L = sum l_t e^(m_t - M), out = sum o_t e^(m_t - M) / L,
- * splits taken in order t = 0, 1, ...; a NaN record makes the output NaN.
+ * the o sum taken in split order t = 0, 1, ... and L by a fixed reduction
+ * tree over t; a NaN record makes the output NaN.
  * Needs split_keys > 0 and the partials tf_attn_rows wrote with the same
  * arguments (TensorFold PR #1653: the paged decode merge, with nonfinite
  * heads kept off the fast path).

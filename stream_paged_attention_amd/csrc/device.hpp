@@ -35,6 +35,21 @@ struct RowsParams {
     float c_log2;          // scale * log2(e): scores are kept in base-2 units
 };
 
+// Loads through the global address space.  Pointers that come out of the
+// segment table are generic; read through them directly the compiler emits
+// flat loads, which count against both the vector-memory and the LDS/scalar
+// wait counters and make it wait for every load in flight (including
+// prefetched ones) before the first use of any.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <typename T>
+__device__ __forceinline__ T load_global(const void *p)
+{
+    return *reinterpret_cast<const __attribute__((address_space(1))) T *>(
+        reinterpret_cast<uintptr_t>(p));
+}
+
 // v_dot2_f32_bf16: a.x*b.x + a.y*b.y + c with fp32 accumulation.
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
 {
@@ -62,6 +77,29 @@ __device__ __forceinline__ uint16_t bf16_out(float x)
     return __builtin_isfinite(x) ? bf16_rne(x) : kBf16NaN;
 }
 
+// max / min as one v_med3_f32 (median of x, y and +-inf).  fmaxf / fminf
+// compile to v_max / v_min plus a canonicalising v_max x, x on each input,
+// three instructions; here NaN behaviour is irrelevant (a NaN score is
+// caught through the softmax sum).
+__device__ __forceinline__ float max2(float x, float y) { return __builtin_amdgcn_fmed3f(x, y, INFINITY); }
+__device__ __forceinline__ float min2(float x, float y) { return __builtin_amdgcn_fmed3f(x, y, -INFINITY); }
+
+// Cross-row lane exchanges (gfx950): v_permlane16_swap / v_permlane32_swap
+// on two copies of x give, summed (or maxed), x combined with the lane 16
+// (resp. 32) apart, in every lane.
+__device__ __forceinline__ void swap16(float x, float &a, float &b)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+    a = __int_as_float(r[0]);
+    b = __int_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float x, float &a, float &b)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    a = __int_as_float(r[0]);
+    b = __int_as_float(r[1]);
+}
+
 // v_exp_f32 (2^x).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -71,6 +109,9 @@ __device__ __forceinline__ float dpp(float x)
 {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
+
+// Lane rotation by 8 inside a 16-lane row (DPP row_ror:8).
+__device__ __forceinline__ float ror8(float x) { return dpp<0x128>(x); }
 
 // Sum over the 16 lanes of a DPP row; every lane of the row receives it.
 // quad_perm(1,0,3,2), quad_perm(2,3,0,1), row_half_mirror, row_mirror.

@@ -7,22 +7,27 @@
 // streams' rows from the segment table; PR #1562: each row's ring, slots and
 // segment come from the table).
 //
-// Inside a work item the split's keys are cut into tiles of TK keys (one
-// tile never crosses a page: pages hold whole tiles, PR #1653).  Wave w
-// takes tiles w, w+4, w+8, ...  A wave step covers 4 keys: lanes 16*kg ..
-// 16*kg+15 hold key kg, each lane D/16 of its dimensions, loaded straight
-// from HBM with 8- or 16-byte loads so that one wave load instruction reads
-// 4 whole consecutive key rows (1 KB at D = 128).  The next tile's loads are
-// issued before the current tile is folded (the ring's slot groups in flight
-// one ahead, PR #1562).  The page id of every tile a wave will read is
-// fetched once, one lane per tile, and taken out with readlane (the per-chunk
-// page lookup hoisted out of the key loop, PR #1653).
+// Inside a work item the split's keys are cut into tiles of TK keys (a tile
+// never crosses a page: pages hold whole tiles, PR #1653).  Wave w takes
+// tiles w, w+4, w+8, ...  A wave step covers 64/LPK keys: the LPK lanes of a
+// key group hold one key, D/LPK of its dimensions each, loaded straight from
+// HBM with 16-byte loads so that one wave load instruction reads whole
+// 128-byte lines of consecutive keys.  The next tile's loads are issued
+// before the current tile is folded (the ring's slot groups in flight one
+// ahead, PR #1562).  The page id of every tile a wave will read is fetched
+// once, one lane per tile, and taken out with readlane (the per-chunk page
+// lookup hoisted out of the key loop, PR #1653).
 //
-// Scores: v_dot2_f32_bf16 on packed bf16 pairs, then a 16-lane DPP row sum.
-// Each 16-lane key group keeps its own online-softmax state (max, sum, o)
-// per query vector; at the end the four key groups of a wave are merged with
-// lane shuffles and the four waves through LDS, always in the same order, so
-// the bits of a (row, head) depend only on its own segment.
+// Scores: v_dot2_f32_bf16 on packed bf16 pairs, then a DPP sum over the key
+// group.  Online softmax per query vector with a wave-wide reference m (raw
+// score units): weights are 2^((s - m) c), c = scale * log2(e), summed into
+// l and, times v, into o per key group.  The reference is raised only when a
+// score exceeds it by more than 8 / c (so weights stay <= 2^8), decided for
+// the whole wave at once and set to the wave's max, so most tiles need no
+// rescale and every key group of a wave shares m: at the end their l and o
+// are plain sums (DPP and lane-swap exchanges), the waves are merged through
+// LDS in wave order, and the bits of a (row, head) depend only on its own
+// segment.  Each lane also keeps the smallest counted score, to see a -inf.
 #include "device.hpp"
 
 namespace tfa {
@@ -31,69 +36,69 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr float kLazy = 8.0f;   // log2 of the largest weight a stale reference may give
 
-// Tile shape.  Each lane holds 64 bytes of a tile's K (and 64 of its V):
-// a wave's K tile is 4 KB (16 keys at D = 128, 8 at D = 256, 32 at D = 64),
-// half that when a pass serves 8 query vectors, so that two K/V tiles in
-// flight, the scores and the accumulators stay in registers.
+// Shape of one pass: LPK lanes per key, DPL dims per lane, NS wave steps of
+// KPS keys per tile, CH tiles in flight per wave.  8 lanes per key where the
+// accumulators fit (3 DPP steps per 8 keys), 16 otherwise.
 template <int D, int QT>
 struct Geo {
-    static constexpr int W = D / 32;                  // packed bf16 pairs per lane per key
-    static constexpr int DPL = D / 16;                // dims per lane
-    static constexpr int NS_BASE = 512 / D;           // wave steps (4 keys each) at 64 B / lane
-    static constexpr int NS = (QT <= 4 || NS_BASE == 1) ? NS_BASE : NS_BASE / 2;
-    static constexpr int TK = 4 * NS;                 // keys per tile
+    static constexpr int LPK = (D == 256 || (D == 128 && QT > 4)) ? 16 : 8;
+    static constexpr int KPS = 64 / LPK;              // keys per wave step
+    static constexpr int DPL = D / LPK;               // dims per lane
+    static constexpr int W = DPL / 2;                 // packed bf16 pairs per lane per key
+    static constexpr int NS = (DPL <= 8) ? 2 : 1;     // wave steps per tile
+    static constexpr int TK = NS * KPS;               // keys per tile
+    static constexpr int CH = 2;                      // tiles in flight per wave
+    static_assert(DPL == 4 || DPL % 8 == 0, "lane slice must be 8 bytes or whole 16-byte chunks");
 };
 
-// Dimension held by lane sub-index sl in pair w, half hh (K, V, q and o agree).
-template <int D>
-__device__ __forceinline__ int lane_dim(int sl, int w, int hh)
+// Dimension of element e (0 .. DPL-1) of lane sub-index sl: 16-byte chunk c
+// covers dims c*8*LPK + sl*8 .. +8, so a chunk's load reads 8*LPK contiguous
+// dims (one or more whole 128-byte lines) across the key group.
+template <int D, int QT>
+__device__ __forceinline__ int lane_dim(int sl, int e)
 {
-    if constexpr (D == 64)
-        return sl * 4 + 2 * w + hh;
-    else if constexpr (D == 128)
-        return sl * 8 + 2 * w + hh;
+    using G = Geo<D, QT>;
+    if constexpr (G::DPL == 4)
+        return sl * 4 + e;
     else
-        return (w >> 2) * 128 + sl * 8 + 2 * (w & 3) + hh;
+        return (e >> 3) * (8 * G::LPK) + sl * 8 + (e & 7);
 }
 
-template <int D>
-__device__ __forceinline__ void load_row(uint32_t (&r)[D / 32], const uint16_t *row, int sl)
+// Load the lane's slice of one key row: base is uniform across the wave
+// (SGPR pair), off a 32-bit byte offset, so the loads use the global
+// SGPR-base form with immediate offsets for the chunks.
+template <int D, int QT>
+__device__ __forceinline__ void load_row(uint32_t *r, const char *base, uint32_t off)
 {
-    if constexpr (D == 64) {
-        const uint2 x = *reinterpret_cast<const uint2 *>(row + sl * 4);
+    using G = Geo<D, QT>;
+    if constexpr (G::DPL == 4) {
+        const u32x2_t x = load_global<u32x2_t>(base + off);
         r[0] = x.x;
         r[1] = x.y;
-    } else if constexpr (D == 128) {
-        const uint4 x = *reinterpret_cast<const uint4 *>(row + sl * 8);
-        r[0] = x.x;
-        r[1] = x.y;
-        r[2] = x.z;
-        r[3] = x.w;
     } else {
-        const uint4 x = *reinterpret_cast<const uint4 *>(row + sl * 8);
-        const uint4 y = *reinterpret_cast<const uint4 *>(row + 128 + sl * 8);
-        r[0] = x.x;
-        r[1] = x.y;
-        r[2] = x.z;
-        r[3] = x.w;
-        r[4] = y.x;
-        r[5] = y.y;
-        r[6] = y.z;
-        r[7] = y.w;
+#pragma unroll
+        for (int c = 0; c < G::DPL / 8; ++c) {
+            const u32x4_t x = load_global<u32x4_t>(base + off + c * 16 * G::LPK);
+            r[4 * c] = x.x;
+            r[4 * c + 1] = x.y;
+            r[4 * c + 2] = x.z;
+            r[4 * c + 3] = x.w;
+        }
     }
 }
 
-// Store the lane's D/16 fp32 values (in lane_dim order) at dst[lane_dim(..)].
-template <int D>
-__device__ __forceinline__ void store_f32(float *dst, const float (&o)[D / 16], int sl)
+template <int D, int QT>
+__device__ __forceinline__ void store_f32(float *dst, const float *o, int sl)
 {
-    if constexpr (D == 64) {
+    using G = Geo<D, QT>;
+    if constexpr (G::DPL == 4) {
         *reinterpret_cast<float4 *>(dst + sl * 4) = make_float4(o[0], o[1], o[2], o[3]);
     } else {
 #pragma unroll
-        for (int c = 0; c < D / 128; ++c) {
-            float *p = dst + c * 128 + sl * 8;
+        for (int c = 0; c < G::DPL / 8; ++c) {
+            float *p = dst + c * 8 * G::LPK + sl * 8;
             *reinterpret_cast<float4 *>(p) = make_float4(o[8 * c], o[8 * c + 1], o[8 * c + 2], o[8 * c + 3]);
             *reinterpret_cast<float4 *>(p + 4) =
                 make_float4(o[8 * c + 4], o[8 * c + 5], o[8 * c + 6], o[8 * c + 7]);
@@ -101,21 +106,17 @@ __device__ __forceinline__ void store_f32(float *dst, const float (&o)[D / 16], 
     }
 }
 
-template <int D>
-__device__ __forceinline__ void store_bf16(uint16_t *dst, const float (&x)[D / 16], int sl)
+// Sum over the LPK lanes of a key group (DPP: quad swaps, half-row mirror,
+// row mirror); every lane of the group receives the sum.
+template <int LPK>
+__device__ __forceinline__ float group_sum(float x)
 {
-    uint32_t w[D / 32];
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i)
-        w[i] = (uint32_t)bf16_out(x[2 * i]) | ((uint32_t)bf16_out(x[2 * i + 1]) << 16);
-    if constexpr (D == 64) {
-        *reinterpret_cast<uint2 *>(dst + sl * 4) = make_uint2(w[0], w[1]);
-    } else {
-#pragma unroll
-        for (int c = 0; c < D / 128; ++c)
-            *reinterpret_cast<uint4 *>(dst + c * 128 + sl * 8) =
-                make_uint4(w[4 * c], w[4 * c + 1], w[4 * c + 2], w[4 * c + 3]);
-    }
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    if constexpr (LPK == 16)
+        x += dpp<0x140>(x);
+    return x;
 }
 
 struct Seg {
@@ -125,48 +126,82 @@ struct Seg {
     int capacity, first, row_offset, n_rows, key_count, partial_offset;
 };
 
-// Element offset of this lane's key row for wave step j of a tile.  PAGED:
-// the tile lies inside one page, so every row of it is in bounds.  CONTIG
-// and RING: keys past the last one are clamped to it (in bounds; the fold
-// ignores them).  RING: slot = first + key, wrapped by one compare-and-
-// subtract (first < slots and key < key_count <= slots).
-template <int D, int KIND>
+// Where wave step j of a tile reads this lane's key row: a uniform base
+// (the kv head's run inside the tile's page, or the head's row 0 / slot 0)
+// plus a 32-bit byte offset.  PAGED: the tile lies inside one page, so every
+// row is in bounds.  CONTIG and RING: keys past the last one are clamped to
+// it (in bounds; the masked fold ignores them).  RING: slot = first + key,
+// wrapped by one compare-and-subtract (first < slots, key < key_count <= slots).
+template <int D, int QT, int KIND>
 struct Addr {
-    size_t base;   // PAGED: offset of key (tile_k0 + kg); CONTIG: kv head's row 0
-    size_t head;   // RING: offset of the kv head's slot 0
-    int first;     // CONTIG / RING: key (tile_k0 + kg)
-    int last;      // CONTIG / RING: last valid key
-    int ring0;     // RING: slot of logical key 0
+    const char *kbase;
+    const char *vbase;
+    uint32_t off0;   // PAGED: byte offset of the lane's first row and slice
+    int first;       // CONTIG / RING: the lane's first key
+    int last;        // CONTIG / RING: last valid key
+    int ring0;       // RING: slot of logical key 0
     int cap;
+    uint32_t lane_b; // byte offset of the lane's slice within a row
 
-    __device__ __forceinline__ size_t at(int j) const
+    __device__ __forceinline__ uint32_t at(int j) const
     {
+        constexpr int KPS = Geo<D, QT>::KPS;
+        constexpr uint32_t ROW = D * 2;
         if constexpr (KIND == TF_KV_PAGED) {
-            return base + (size_t)(4 * j) * D;
+            return off0 + (uint32_t)(KPS * j) * ROW;
         } else if constexpr (KIND == TF_KV_CONTIG) {
-            return base + (size_t)min(first + 4 * j, last) * D;
+            return (uint32_t)min(first + KPS * j, last) * ROW + lane_b;
         } else {
-            int slot = ring0 + min(first + 4 * j, last);
+            int slot = ring0 + min(first + KPS * j, last);
             slot -= (slot >= cap) ? cap : 0;
-            return head + (size_t)slot * D;
+            return (uint32_t)slot * ROW + lane_b;
         }
     }
 };
 
-// Fold one K/V tile into the key group's online-softmax state.  key0 is the
-// lane's first key; with MASKED, key key0 + 4j counts for query vector v only
-// below lim[v] (causal limit and split end) and then contributes exactly
-// nothing, not even a NaN from its value.  chk[v] turns NaN as soon as a
-// counted score is NaN or +-Inf (x * 0 is NaN exactly for those).
+// Per-query-vector online-softmax state.  m, mc and thr are the same in
+// every lane of the wave; lo, l and o belong to the lane's key group.
+template <int D, int QT>
+struct State {
+    float m[QT];    // reference max (raw score units), -inf before the first score
+    float mc[QT];   // m * c, or 0 while m is -inf
+    float thr[QT];  // m + 8 / c: a score above it raises the reference
+    float lo[QT];   // min of the counted scores (-inf flags a -inf score)
+    float l[QT];
+    float o[QT][Geo<D, QT>::DPL];
+};
+
+// Combine a value over the key groups of the wave (lanes LPK apart), result
+// in every lane.
+template <int LPK, bool MAX>
+__device__ __forceinline__ float across_groups(float x)
+{
+    float a, b;
+    if constexpr (LPK == 8)
+        x = MAX ? max2(x, ror8(x)) : x + ror8(x);
+    swap16(x, a, b);
+    x = MAX ? max2(a, b) : a + b;
+    swap32(x, a, b);
+    return MAX ? max2(a, b) : a + b;
+}
+template <int LPK>
+__device__ __forceinline__ float groups_min(float x)
+{
+    return -across_groups<LPK, true>(-x);
+}
+
+// Fold one K/V tile.  key0 is the lane's first key.  With MASKED, key
+// key0 + KPS*j counts for query vector v only below lim[v] (causal limit and
+// split end) and then adds exactly nothing, not even a NaN from its value.
 template <int D, int QT, bool MASKED>
 __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][Geo<D, QT>::W],
                                           const uint32_t (&vb)[Geo<D, QT>::NS][Geo<D, QT>::W],
-                                          const uint32_t (&qr)[QT][Geo<D, QT>::W], float c_log2,
-                                          float (&m)[QT], float (&l)[QT],
-                                          float (&o)[QT][Geo<D, QT>::DPL], float (&chk)[QT],
-                                          int key0, const int (&lim)[QT])
+                                          const uint32_t (&qr)[QT][Geo<D, QT>::W], float c,
+                                          float lazy, State<D, QT> &st, int key0,
+                                          const int (&lim)[QT])
 {
-    constexpr int NS = Geo<D, QT>::NS, W = Geo<D, QT>::W, DPL = Geo<D, QT>::DPL;
+    using G = Geo<D, QT>;
+    constexpr int NS = G::NS, W = G::W, DPL = G::DPL, KPS = G::KPS;
     float s[QT][NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
@@ -176,37 +211,53 @@ __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][G
 #pragma unroll
             for (int w = 0; w < W; ++w)
                 a = dot2_bf16(qr[v][w], kb[j][w], a);
-            s[v][j] = row16_sum(a) * c_log2;
+            s[v][j] = group_sum<G::LPK>(a);
+        }
+    }
+    bool need = false;
+#pragma unroll
+    for (int v = 0; v < QT; ++v) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            if constexpr (MASKED) {
+                const bool vis = key0 + KPS * j < lim[v];
+                st.lo[v] = min2(st.lo[v], vis ? s[v][j] : INFINITY);
+                s[v][j] = vis ? s[v][j] : -INFINITY;
+            } else {
+                st.lo[v] = min2(st.lo[v], s[v][j]);
+            }
+            need |= s[v][j] > st.thr[v];
+        }
+    }
+    // raise the reference to the wave's max when some score passed it
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+        for (int v = 0; v < QT; ++v) {
+            float t = s[v][0];
+#pragma unroll
+            for (int j = 1; j < NS; ++j)
+                t = max2(t, s[v][j]);
+            t = __builtin_amdgcn_readfirstlane(__float_as_int(across_groups<G::LPK, true>(t)));
+            const float tm = __int_as_float((int)t);
+            // only a query vector whose own max passed its reference moves;
+            // one that saw nothing (all masked) keeps m = -inf and mc = 0
+            const bool up = tm > st.m[v];
+            const float alpha = up ? exp2_fast((st.m[v] - tm) * c) : 1.0f;
+            st.m[v] = up ? tm : st.m[v];
+            st.mc[v] = up ? tm * c : st.mc[v];
+            st.thr[v] = up ? tm + lazy : st.thr[v];
+            st.l[v] *= alpha;
+#pragma unroll
+            for (int d = 0; d < DPL; ++d)
+                st.o[v][d] *= alpha;
         }
     }
 #pragma unroll
     for (int v = 0; v < QT; ++v) {
-        float mt = -INFINITY;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            float x = s[v][j];
-            if constexpr (MASKED) {
-                const bool vis = key0 + 4 * j < lim[v];
-                chk[v] = fmaf(vis ? x : 0.0f, 0.0f, chk[v]);
-                x = vis ? x : -INFINITY;
-                s[v][j] = x;
-            } else {
-                chk[v] = fmaf(x, 0.0f, chk[v]);
-            }
-            mt = fmaxf(mt, x);
-        }
-        const float mn = fmaxf(m[v], mt);
-        const float ms = (mn == -INFINITY) ? 0.0f : mn;
-        const float alpha = exp2_fast(m[v] - ms);
-        m[v] = mn;
-        l[v] *= alpha;
-#pragma unroll
-        for (int d = 0; d < DPL; ++d)
-            o[v][d] *= alpha;
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            const float p = exp2_fast(s[v][j] - ms);
-            l[v] += p;
+            const float p = exp2_fast(fmaf(s[v][j], c, -st.mc[v]));
+            st.l[v] += p;
             s[v][j] = p;
         }
     }
@@ -221,15 +272,16 @@ __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][G
 #pragma unroll
         for (int v = 0; v < QT; ++v) {
             if constexpr (MASKED) {
-                if (key0 + 4 * j < lim[v]) {
+                // a key this query vector may not see has p = 0; its value is
+                // replaced by 0 too, so a NaN there cannot leak in
+                const bool vis = key0 + KPS * j < lim[v];
 #pragma unroll
-                    for (int d = 0; d < DPL; ++d)
-                        o[v][d] = fmaf(s[v][j], vf[d], o[v][d]);
-                }
+                for (int d = 0; d < DPL; ++d)
+                    st.o[v][d] = fmaf(s[v][j], vis ? vf[d] : 0.0f, st.o[v][d]);
             } else {
 #pragma unroll
                 for (int d = 0; d < DPL; ++d)
-                    o[v][d] = fmaf(s[v][j], vf[d], o[v][d]);
+                    st.o[v][d] = fmaf(s[v][j], vf[d], st.o[v][d]);
             }
         }
     }
@@ -238,7 +290,9 @@ __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][G
 template <int D, int KIND, int QT>
 __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
 {
-    constexpr int W = Geo<D, QT>::W, DPL = Geo<D, QT>::DPL, TK = Geo<D, QT>::TK, NS = Geo<D, QT>::NS;
+    using G = Geo<D, QT>;
+    constexpr int W = G::W, DPL = G::DPL, TK = G::TK, NS = G::NS, LPK = G::LPK, CH = G::CH;
+    // per wave and query vector: m, mx, lo, l, o[D]
     __shared__ float xw[kWaves][QT][D + 4];
 
     const int seg_i = blockIdx.x / p.n_split_max;
@@ -246,8 +300,8 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
     const int g = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int kg = lane >> 4;
-    const int sl = lane & 15;
+    const int kg = lane / LPK;
+    const int sl = lane % LPK;
 
     const tf_segment &sd = p.segs[seg_i];
     Seg s;
@@ -262,7 +316,6 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
     s.partial_offset = sd.partial_offset;
 
     // ---- per-segment checks (identical in every work item of the segment)
-    int errbits = 0;
     const bool rows_ok = s.n_rows >= 1 && s.n_rows <= s.key_count && s.row_offset >= 0 &&
                          (int64_t)s.row_offset + s.n_rows <= p.total_rows;
     if (!rows_ok) {
@@ -271,6 +324,7 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
             report(p.err, TF_ERR_BAD_ROWS);
         return;
     }
+    int errbits = 0;
     if constexpr (KIND == TF_KV_PAGED) {
         if (s.pages == nullptr || s.capacity < 0 ||
             (int64_t)s.key_count > ((int64_t)s.capacity << p.page_shift))
@@ -283,8 +337,7 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
         if (s.first < 0 || s.first >= s.capacity)
             errbits |= TF_ERR_BAD_RING;
     }
-    const int kc = s.key_count > 0 ? s.key_count : 1;
-    const int n_splits = p.split_keys > 0 ? (kc + p.split_keys - 1) / p.split_keys : 1;
+    const int n_splits = p.split_keys > 0 ? (s.key_count + p.split_keys - 1) / p.split_keys : 1;
     if (t >= n_splits)
         return;   // block-uniform: this grid cell has no split of this segment
     bool parts_ok = true;
@@ -301,26 +354,31 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
     const int k_end = p.split_keys > 0 ? min(k0 + p.split_keys, s.key_count) : s.key_count;
     const int n_tiles = errbits ? 0 : (k_end - k0 + TK - 1) / TK;
     const int my_tiles = n_tiles > wave ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
+    const float c = p.c_log2;
+    const float lazy = kLazy / p.c_log2;
 
     for (int qt0 = 0; qt0 < nq; qt0 += QT) {
-        // ---- query vectors of this tile: v -> (row r, head h)
+        // ---- query vectors of this pass: v -> (row r, head h)
         uint32_t qr[QT][W];
         int lim[QT];
-        float m[QT], l[QT], o[QT][DPL];
-        float chk[QT];   // NaN once a counted score was not finite
+        State<D, QT> st;
 #pragma unroll
         for (int v = 0; v < QT; ++v) {
             const int qv = qt0 + v;
             const int r = qv / group;
             const int h = g * group + qv % group;
-            m[v] = -INFINITY;
-            l[v] = 0.0f;
-            chk[v] = 0.0f;
+            st.m[v] = -INFINITY;
+            st.mc[v] = 0.0f;
+            st.thr[v] = -INFINITY;
+            st.lo[v] = INFINITY;
+            st.l[v] = 0.0f;
 #pragma unroll
             for (int d = 0; d < DPL; ++d)
-                o[v][d] = 0.0f;
+                st.o[v][d] = 0.0f;
             if (qv < nq) {
-                load_row<D>(qr[v], p.q + ((size_t)(s.row_offset + r) * p.hq + h) * D, sl);
+                load_row<D, QT>(qr[v], reinterpret_cast<const char *>(p.q) +
+                                           ((size_t)(s.row_offset + r) * p.hq + h) * (D * 2),
+                                (uint32_t)(sl * (G::DPL == 4 ? 8 : 16)));
                 lim[v] = min(s.key_count - s.n_rows + r + 1, k_end);
             } else {
 #pragma unroll
@@ -335,31 +393,37 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
             if (qt0 + v < nq)
                 lim_min = min(lim_min, lim[v]);
 
-        // ---- key tiles of this wave, double-buffered
+        // ---- this wave's key tiles
         bool page_bad = false;
         int pid = 0;
         auto tile_key0 = [&](int i) { return k0 + (wave + kWaves * i) * TK; };
+        // page ids of this wave's tiles i0 .. i0+63, one lane per tile
+        auto load_pids = [&](int i0) {
+            if constexpr (KIND == TF_KV_PAGED) {
+                const int ti = i0 + lane;
+                pid = ti < my_tiles ? load_global<int32_t>(s.pages + (tile_key0(ti) >> p.page_shift)) : 0;
+            }
+        };
+        const uint32_t lane_b = (uint32_t)sl * (G::DPL == 4 ? 8u : 16u);
         auto setup = [&](int i) {
-            Addr<D, KIND> a;
+            Addr<D, QT, KIND> a;
             const int key = tile_key0(i) + kg;
             a.cap = s.capacity;
+            a.lane_b = lane_b;
             if constexpr (KIND == TF_KV_PAGED) {
-                if ((i & 63) == 0) {
-                    const int ti = i + lane;
-                    pid = ti < my_tiles ? s.pages[tile_key0(ti) >> p.page_shift] : 0;
-                }
                 int page = __builtin_amdgcn_readlane(pid, i & 63);
                 if ((unsigned)page >= (unsigned)p.pool_pages) {
                     page_bad = true;
                     page = 0;
                 }
-                a.base = (((size_t)page * p.hkv + g) * p.page_size + (key & (p.page_size - 1))) * D;
-            } else if constexpr (KIND == TF_KV_CONTIG) {
-                a.base = (size_t)g * s.capacity * D;
-                a.first = key;
-                a.last = s.key_count - 1;
+                const size_t run = ((size_t)page * p.hkv + g) * p.page_size * (D * 2);
+                a.kbase = reinterpret_cast<const char *>(s.k) + run;
+                a.vbase = reinterpret_cast<const char *>(s.v) + run;
+                a.off0 = (uint32_t)(key & (p.page_size - 1)) * (D * 2) + lane_b;
             } else {
-                a.head = (size_t)g * s.capacity * D;
+                const size_t head = (size_t)g * s.capacity * (D * 2);
+                a.kbase = reinterpret_cast<const char *>(s.k) + head;
+                a.vbase = reinterpret_cast<const char *>(s.v) + head;
                 a.first = key;
                 a.last = s.key_count - 1;
                 a.ring0 = s.first;
@@ -368,74 +432,95 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
         };
         // Loads are unconditional: a key at or past k_end is read from an
         // in-bounds address (its own page for PAGED, the last key for
-        // CONTIG/RING) and then excluded by the masked fold, which never
-        // lets such a key's score or value reach the state.
+        // CONTIG/RING) and then excluded by the masked fold.
         auto load_tile = [&](uint32_t (&kb)[NS][W], uint32_t (&vb)[NS][W], int i) {
-            const Addr<D, KIND> a = setup(i);
+            const Addr<D, QT, KIND> a = setup(i);
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
-                const size_t off = a.at(j);
-                load_row<D>(kb[j], s.k + off, sl);
-                load_row<D>(vb[j], s.v + off, sl);
+                const uint32_t off = a.at(j);
+                load_row<D, QT>(kb[j], a.kbase, off);
             }
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                const uint32_t off = a.at(j);
+                load_row<D, QT>(vb[j], a.vbase, off);
+            }
+            // keep the issue order tile by tile (K, then V): the waits before
+            // each fold count loads in issue order
+            __builtin_amdgcn_sched_barrier(0);
         };
         // Full tiles (every key visible to every query vector of the pass)
-        // come first in key order; the masked tail (split end, causal rows)
-        // is folded by a separate loop so that the fast loop carries no
-        // per-key masks.
+        // come first in key order and run through a rolling pipeline: CH
+        // tiles are in flight, and as soon as tile i is folded its registers
+        // take the loads of tile i + CH.  Loads past the last full tile
+        // repeat it (an L2 hit, not HBM traffic) so that every wait before a
+        // fold is an exact count in issue order.  The masked tail (split
+        // end, causal rows) is folded one tile at a time by its own loop.
         const int n_full = max(0, min(n_tiles, (lim_min - k0) / TK));
         const int my_full = n_full > wave ? (n_full - wave + kWaves - 1) / kWaves : 0;
-        for (int i = 0; i < my_full; ++i) {
-            uint32_t kb[NS][W], vb[NS][W];
-            load_tile(kb, vb, i);
-            fold_tile<D, QT, false>(kb, vb, qr, p.c_log2, m, l, o, chk, tile_key0(i) + kg, lim);
+        for (int b0 = 0; b0 < my_full; b0 += 64) {
+            // page ids for this batch first, so no load other than K/V is in
+            // flight inside the pipeline (a wait for one would drain it)
+            load_pids(b0);
+            const int b1 = min(my_full, b0 + 64);
+            uint32_t kb[CH][NS][W], vb[CH][NS][W];
+#pragma unroll
+            for (int u = 0; u < CH; ++u)
+                load_tile(kb[u], vb[u], min(b0 + u, b1 - 1));
+            for (int i0 = b0; i0 < b1; i0 += CH) {
+#pragma unroll
+                for (int u = 0; u < CH; ++u) {
+                    const int i = i0 + u;
+                    if (i < b1)
+                        fold_tile<D, QT, false>(kb[u], vb[u], qr, c, lazy, st, tile_key0(i) + kg, lim);
+                    load_tile(kb[u], vb[u], min(i + CH, b1 - 1));
+                }
+            }
         }
         for (int i = my_full; i < my_tiles; ++i) {
+            if (i == my_full || (i & 63) == 0)
+                load_pids(i & ~63);
             uint32_t kb[NS][W], vb[NS][W];
             load_tile(kb, vb, i);
-            fold_tile<D, QT, true>(kb, vb, qr, p.c_log2, m, l, o, chk, tile_key0(i) + kg, lim);
+            fold_tile<D, QT, true>(kb, vb, qr, c, lazy, st, tile_key0(i) + kg, lim);
         }
         if (page_bad) {
             if (lane == 0)
                 report(p.err, TF_ERR_BAD_PAGE);
 #pragma unroll
             for (int v = 0; v < QT; ++v)
-                chk[v] = NAN;
+                st.l[v] = NAN;
         }
 
-        // ---- merge the four key groups of the wave (lanes l, l^16, l^32, l^48)
+        // ---- the key groups of the wave share m: sum l and o, min lo
 #pragma unroll
-        for (int off = 16; off <= 32; off <<= 1) {
+        for (int v = 0; v < QT; ++v) {
+            st.l[v] = across_groups<LPK, false>(st.l[v]);
+            st.lo[v] = groups_min<LPK>(st.lo[v]);
 #pragma unroll
-            for (int v = 0; v < QT; ++v) {
-                const float mb = __shfl_xor(m[v], off);
-                const float lb = __shfl_xor(l[v], off);
-                const float cb = __shfl_xor(chk[v], off);
-                float mn, fa, fb;
-                merge_scales(m[v], mb, mn, fa, fb);
-                m[v] = mn;
-                l[v] = l[v] * fa + lb * fb;
-                chk[v] += cb;
+            for (int d = 0; d < DPL; d += 4) {
 #pragma unroll
-                for (int d = 0; d < DPL; ++d) {
-                    const float ob = __shfl_xor(o[v][d], off);
-                    o[v][d] = o[v][d] * fa + ob * fb;
-                }
+                for (int e = d; e < d + 4; ++e)
+                    st.o[v][e] = across_groups<LPK, false>(st.o[v][e]);
+                // a few values at a time: keeps the exchange temporaries few
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 
         // ---- every wave parks its state in LDS; then all threads finalise
-        // (query vector, dimension pairs), merging the waves in wave order
-        if (lane < 16) {
+        // (query vector, dimension pair) elements, merging the waves in wave
+        // order and renormalising to the true max
+        if (lane < LPK) {
 #pragma unroll
             for (int v = 0; v < QT; ++v) {
                 float *rec = xw[wave][v];
                 if (lane == 0) {
-                    rec[0] = m[v];
-                    rec[1] = l[v];
-                    rec[2] = chk[v];
+                    rec[0] = st.m[v];
+                    rec[1] = 0.0f;
+                    rec[2] = st.lo[v];
+                    rec[3] = st.l[v];
                 }
-                store_f32<D>(rec + 4, o[v], sl);
+                store_f32<D, QT>(rec + 4, st.o[v], sl);
             }
         }
         __syncthreads();
@@ -445,21 +530,24 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
             const int qv = qt0 + v;
             if (qv >= nq)
                 break;   // e only grows with v
-            float mm = xw[0][v][0], ll = xw[0][v][1], cc = xw[0][v][2];
+            float mm = xw[0][v][0], lw = xw[0][v][2], ll = xw[0][v][3];
             float o0 = xw[0][v][4 + d], o1 = xw[0][v][5 + d];
 #pragma unroll
             for (int w = 1; w < kWaves; ++w) {
-                float mn, fa, fb;
-                merge_scales(mm, xw[w][v][0], mn, fa, fb);
+                const float mb = xw[w][v][0];
+                const float mn = max2(mm, mb);
+                const float ms = (mn == -INFINITY) ? 0.0f : mn;
+                const float fa = exp2_fast((mm - ms) * c);
+                const float fb = exp2_fast((mb - ms) * c);
                 mm = mn;
-                ll = ll * fa + xw[w][v][1] * fb;
-                cc += xw[w][v][2];
+                lw = min2(lw, xw[w][v][2]);
+                ll = ll * fa + xw[w][v][3] * fb;
                 o0 = o0 * fa + xw[w][v][4 + d] * fb;
                 o1 = o1 * fa + xw[w][v][5 + d] * fb;
             }
             const int r = qv / group;
             const int h = g * group + qv % group;
-            const bool nan_out = __builtin_isnan(cc) || errbits != 0;
+            const bool nan_out = __builtin_isnan(ll) || lw == -INFINITY || errbits != 0;
             if (p.split_keys > 0) {
                 if (!parts_ok)
                     continue;
@@ -467,7 +555,7 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
                 float *rec = p.partials + recno * (D + 4);
                 if (d == 0)
                     *reinterpret_cast<float4 *>(rec) =
-                        make_float4(nan_out ? NAN : mm * kLn2, nan_out ? NAN : ll, 0.0f, 0.0f);
+                        make_float4(nan_out ? NAN : mm * (c * kLn2), nan_out ? NAN : ll, 0.0f, 0.0f);
                 *reinterpret_cast<float2 *>(rec + 4 + d) =
                     make_float2(nan_out ? NAN : o0, nan_out ? NAN : o1);
             } else {
