@@ -138,7 +138,7 @@ typedef struct tf_attn_args {
     int32_t pool_pages;       /* PAGED: pages in the pool (page ids are checked against it)  */
     int32_t split_keys;       /* keys per partial (multiple of 32), or 0 = one split: then
                                  tf_attn_rows writes out directly and needs no partials      */
-    float scale;              /* score = scale * (q . k), normally 1 / sqrt(head_dim)        */
+    float scale;              /* score = scale * (q . k), finite and > 0, normally 1/sqrt(D) */
     const tf_segment *segs;   /* device: n_segments entries                                  */
     const void *q;            /* device bf16 [total_rows][n_q_heads][head_dim]               */
     void *out;                /* device bf16 [total_rows][n_q_heads][head_dim]               */

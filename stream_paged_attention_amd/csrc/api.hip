@@ -50,7 +50,7 @@ int check_args(const tf_attn_args *a, bool need_partials)
     }
     if (a->split_keys < 0 || a->split_keys % 32 != 0)
         return TF_E_UNSUPPORTED;
-    if (!(a->scale == a->scale))
+    if (!(a->scale > 0.0f && a->scale < 3.0e38f))   // also refuses NaN and +inf
         return TF_E_INVALID;
     if (a->n_segments == 0)
         return TF_OK;

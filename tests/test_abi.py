@@ -100,7 +100,7 @@ def _args(**kw):
     a.page_size = kw.get("page_size", 32)
     a.pool_pages = kw.get("pool_pages", 10)
     a.split_keys = kw.get("split", 0)
-    a.scale = 0.088
+    a.scale = kw.get("scale", 0.088)
     fake = 0x10000  # 16-byte aligned stand-in addresses: nothing is dereferenced
     a.segs = kw.get("segs", fake)
     a.q = kw.get("q", fake)
@@ -123,6 +123,10 @@ def _args(**kw):
     (dict(max_keys=1, max_rows=2), binding.TF_E_INVALID),
     (dict(pool_pages=0), binding.TF_E_INVALID),
     (dict(split=512), binding.TF_E_WORKSPACE),        # partials missing
+    (dict(scale=0.0), binding.TF_E_INVALID),
+    (dict(scale=-0.1), binding.TF_E_INVALID),
+    (dict(scale=float("inf")), binding.TF_E_INVALID),
+    (dict(scale=float("nan")), binding.TF_E_INVALID),
 ])
 def test_rows_refuses_bad_scalars_without_launching(kw, rc):
     # stream 0 and fake pointers: a refused call must return before any launch
