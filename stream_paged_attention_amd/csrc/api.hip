@@ -211,6 +211,9 @@ int tf_attn_rows(const tf_attn_args *a, hipStream_t stream)
     if (a->n_segments == 0)
         return TF_OK;
     const tfa::RowsParams p = make_params(a);
+    // one block per (split, segment, kv head), in a one-dimensional grid
+    if ((int64_t)p.n_split_max * p.n_segments * p.hkv > (int64_t)INT32_MAX / 256)
+        return TF_E_UNSUPPORTED;
     const int nq_max = a->max_rows * p.group;
     const int qt = nq_max <= 4 ? 4 : 8;
     if (tfa::launch_rows_valu(p, a->head_dim, a->kind, qt, stream) != hipSuccess)

@@ -50,6 +50,14 @@ __device__ __forceinline__ T load_global(const void *p)
         reinterpret_cast<uintptr_t>(p));
 }
 
+// Streaming load (non-temporal hint): K/V rows are read once per launch.
+template <typename T>
+__device__ __forceinline__ T load_stream(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) T *>(
+        reinterpret_cast<uintptr_t>(p)));
+}
+
 // v_dot2_f32_bf16: a.x*b.x + a.y*b.y + c with fp32 accumulation.
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
 {

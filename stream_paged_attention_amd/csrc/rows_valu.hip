@@ -50,6 +50,11 @@ struct Geo {
     static constexpr int NS = (DPL <= 8) ? 2 : 1;     // wave steps per tile
     static constexpr int TK = NS * KPS;               // keys per tile
     static constexpr int CH = 2;                      // tiles in flight per wave
+    // Partial sums parked in LDS per wave and query vector: one per 16-lane
+    // row (R = 4), or per row pair / per wave (R = 2, 1) where 4 would not
+    // fit in 32 KB per workgroup.
+    static constexpr int R4_BYTES = kWaves * QT * 4 * D * 4;
+    static constexpr int R = R4_BYTES <= 32768 ? 4 : (R4_BYTES / 2 <= 32768 ? 2 : 1);
     static_assert(DPL == 4 || DPL % 8 == 0, "lane slice must be 8 bytes or whole 16-byte chunks");
 };
 
@@ -69,18 +74,19 @@ __device__ __forceinline__ int lane_dim(int sl, int e)
 // Load the lane's slice of one key row: base is uniform across the wave
 // (SGPR pair), off a 32-bit byte offset, so the loads use the global
 // SGPR-base form with immediate offsets for the chunks.
-template <int D, int QT>
+template <int D, int QT, bool STREAM = false>
 __device__ __forceinline__ void load_row(uint32_t *r, const char *base, uint32_t off)
 {
     using G = Geo<D, QT>;
     if constexpr (G::DPL == 4) {
-        const u32x2_t x = load_global<u32x2_t>(base + off);
+        const u32x2_t x = STREAM ? load_stream<u32x2_t>(base + off) : load_global<u32x2_t>(base + off);
         r[0] = x.x;
         r[1] = x.y;
     } else {
 #pragma unroll
         for (int c = 0; c < G::DPL / 8; ++c) {
-            const u32x4_t x = load_global<u32x4_t>(base + off + c * 16 * G::LPK);
+            const char *a = base + off + c * 16 * G::LPK;
+            const u32x4_t x = STREAM ? load_stream<u32x4_t>(a) : load_global<u32x4_t>(a);
             r[4 * c] = x.x;
             r[4 * c + 1] = x.y;
             r[4 * c + 2] = x.z;
@@ -159,6 +165,11 @@ struct Addr {
     }
 };
 
+__device__ __forceinline__ float uniform(float x)
+{
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
 // Per-query-vector online-softmax state.  m, mc and thr are the same in
 // every lane of the wave; lo, l and o belong to the lane's key group.
 template <int D, int QT>
@@ -214,7 +225,9 @@ __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][G
             s[v][j] = group_sum<G::LPK>(a);
         }
     }
-    bool need = false;
+    // need: lanes holding a score above its reference's threshold, as a
+    // wave mask (each compare writes a lane mask; ORing them is scalar work)
+    uint64_t need = 0;
 #pragma unroll
     for (int v = 0; v < QT; ++v) {
 #pragma unroll
@@ -226,11 +239,11 @@ __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][G
             } else {
                 st.lo[v] = min2(st.lo[v], s[v][j]);
             }
-            need |= s[v][j] > st.thr[v];
+            need |= __builtin_amdgcn_ballot_w64(s[v][j] > st.thr[v]);
         }
     }
     // raise the reference to the wave's max when some score passed it
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    if (need != 0) {
 #pragma unroll
         for (int v = 0; v < QT; ++v) {
             float t = s[v][0];
@@ -243,9 +256,11 @@ __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][G
             // one that saw nothing (all masked) keeps m = -inf and mc = 0
             const bool up = tm > st.m[v];
             const float alpha = up ? exp2_fast((st.m[v] - tm) * c) : 1.0f;
-            st.m[v] = up ? tm : st.m[v];
-            st.mc[v] = up ? tm * c : st.mc[v];
-            st.thr[v] = up ? tm + lazy : st.thr[v];
+            // m, m*c and the threshold are wave-uniform: kept in scalar
+            // registers (readfirstlane), they cost no vector registers
+            st.m[v] = uniform(up ? tm : st.m[v]);
+            st.mc[v] = uniform(up ? tm * c : st.mc[v]);
+            st.thr[v] = uniform(up ? tm + lazy : st.thr[v]);
             st.l[v] *= alpha;
 #pragma unroll
             for (int d = 0; d < DPL; ++d)
@@ -292,14 +307,24 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
 {
     using G = Geo<D, QT>;
     constexpr int W = G::W, DPL = G::DPL, TK = G::TK, NS = G::NS, LPK = G::LPK, CH = G::CH;
-    // per wave and query vector: m, mx, lo, l, o[D]
-    __shared__ float xw[kWaves][QT][D + 4];
+    constexpr int R = G::R;
+    // per wave, query vector and row group: o[D]; l and the smallest score;
+    // per wave and query vector: the reference m
+    __shared__ float xo[kWaves][QT][R][D];
+    __shared__ float xl[kWaves][QT][R][2];
+    __shared__ float xm[kWaves][QT];
 
-    const int seg_i = blockIdx.x / p.n_split_max;
-    const int t = blockIdx.x % p.n_split_max;
-    const int g = blockIdx.y;
+    // Work items in dispatch order: kv head fastest, then segment, split
+    // slowest.  Consecutive blocks go to different XCDs (round robin), so
+    // every XCD gets an even share of each split band; cells past a
+    // segment's last split come late and exit at once.
+    const int g = blockIdx.x % p.hkv;
+    const int seg_i = (blockIdx.x / p.hkv) % p.n_segments;
+    const int t = blockIdx.x / (p.hkv * p.n_segments);
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave index as a scalar: everything derived from it (tile lists, loop
+    // bounds) stays in scalar registers and the loops branch on scalars
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int kg = lane / LPK;
     const int sl = lane % LPK;
 
@@ -438,12 +463,12 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
                 const uint32_t off = a.at(j);
-                load_row<D, QT>(kb[j], a.kbase, off);
+                load_row<D, QT, true>(kb[j], a.kbase, off);
             }
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
                 const uint32_t off = a.at(j);
-                load_row<D, QT>(vb[j], a.vbase, off);
+                load_row<D, QT, true>(vb[j], a.vbase, off);
             }
             // keep the issue order tile by tile (K, then V): the waits before
             // each fold count loads in issue order
@@ -492,36 +517,45 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
                 st.l[v] = NAN;
         }
 
-        // ---- the key groups of the wave share m: sum l and o, min lo
+        // ---- the key groups of a wave share m, so their l and o add up.  A
+        // DPP step folds the two key groups of each 16-lane row (LPK 8),
+        // lane swaps fold rows where fewer than 4 row sums are kept; the
+        // lanes of one copy park their sums in LDS, then all threads finish
+        // (query vector, dimension pair) elements: rows and waves summed in
+        // a fixed order, each wave scaled to the largest reference.
+        auto fold = [&](float x, bool mn) {
+            float a, b;
+            if constexpr (LPK == 8)
+                x = mn ? min2(x, ror8(x)) : x + ror8(x);
+            if constexpr (R <= 2) {
+                swap16(x, a, b);
+                x = mn ? min2(a, b) : a + b;
+            }
+            if constexpr (R == 1) {
+                swap32(x, a, b);
+                x = mn ? min2(a, b) : a + b;
+            }
+            return x;
+        };
+        const bool writer = (LPK == 16 || (lane & 8) == 0) && (R == 4 || (lane & 16) == 0) &&
+                            (R >= 2 || (lane & 32) == 0);
+        const int rg = R == 4 ? (lane >> 4) : (R == 2 ? (lane >> 5) : 0);
 #pragma unroll
         for (int v = 0; v < QT; ++v) {
-            st.l[v] = across_groups<LPK, false>(st.l[v]);
-            st.lo[v] = groups_min<LPK>(st.lo[v]);
+            const float lv = fold(st.l[v], false);
+            const float lov = fold(st.lo[v], true);
 #pragma unroll
-            for (int d = 0; d < DPL; d += 4) {
-#pragma unroll
-                for (int e = d; e < d + 4; ++e)
-                    st.o[v][e] = across_groups<LPK, false>(st.o[v][e]);
-                // a few values at a time: keeps the exchange temporaries few
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-
-        // ---- every wave parks its state in LDS; then all threads finalise
-        // (query vector, dimension pair) elements, merging the waves in wave
-        // order and renormalising to the true max
-        if (lane < LPK) {
-#pragma unroll
-            for (int v = 0; v < QT; ++v) {
-                float *rec = xw[wave][v];
-                if (lane == 0) {
-                    rec[0] = st.m[v];
-                    rec[1] = 0.0f;
-                    rec[2] = st.lo[v];
-                    rec[3] = st.l[v];
+            for (int d = 0; d < DPL; ++d)
+                st.o[v][d] = fold(st.o[v][d], false);
+            if (writer) {
+                store_f32<D, QT>(xo[wave][v][rg], st.o[v], sl);
+                if (sl == 0) {
+                    xl[wave][v][rg][0] = lv;
+                    xl[wave][v][rg][1] = lov;
                 }
-                store_f32<D, QT>(rec + 4, st.o[v], sl);
             }
+            if (lane == 0)
+                xm[wave][v] = st.m[v];
         }
         __syncthreads();
         for (int e = threadIdx.x; e < QT * (D / 2); e += kThreads) {
@@ -530,20 +564,27 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
             const int qv = qt0 + v;
             if (qv >= nq)
                 break;   // e only grows with v
-            float mm = xw[0][v][0], lw = xw[0][v][2], ll = xw[0][v][3];
-            float o0 = xw[0][v][4 + d], o1 = xw[0][v][5 + d];
+            float mm = xm[0][v];
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w) {
-                const float mb = xw[w][v][0];
-                const float mn = max2(mm, mb);
-                const float ms = (mn == -INFINITY) ? 0.0f : mn;
-                const float fa = exp2_fast((mm - ms) * c);
-                const float fb = exp2_fast((mb - ms) * c);
-                mm = mn;
-                lw = min2(lw, xw[w][v][2]);
-                ll = ll * fa + xw[w][v][3] * fb;
-                o0 = o0 * fa + xw[w][v][4 + d] * fb;
-                o1 = o1 * fa + xw[w][v][5 + d] * fb;
+            for (int w = 1; w < kWaves; ++w)
+                mm = max2(mm, xm[w][v]);
+            const float ms = (mm == -INFINITY) ? 0.0f : mm;
+            float ll = 0.0f, lw = INFINITY, o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float f = exp2_fast((xm[w][v] - ms) * c);
+                float lr = 0.0f, a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+                for (int q = 0; q < R; ++q) {
+                    lr += xl[w][v][q][0];
+                    lw = min2(lw, xl[w][v][q][1]);
+                    const float2 x = *reinterpret_cast<const float2 *>(&xo[w][v][q][d]);
+                    a0 += x.x;
+                    a1 += x.y;
+                }
+                ll = fmaf(lr, f, ll);
+                o0 = fmaf(a0, f, o0);
+                o1 = fmaf(a1, f, o1);
             }
             const int r = qv / group;
             const int h = g * group + qv % group;
@@ -603,10 +644,10 @@ hipError_t launch_kind(const RowsParams &p, int kind, int qt, dim3 grid, hipStre
 
 }  // namespace
 
-// Launch the VALU rows kernel; grid = (n_segments * n_split_max, n_kv_heads).
+// Launch the VALU rows kernel; one block per (split, segment, kv head).
 hipError_t launch_rows_valu(const RowsParams &p, int head_dim, int kind, int qt, hipStream_t st)
 {
-    const dim3 grid((unsigned)(p.n_segments * p.n_split_max), (unsigned)p.hkv);
+    const dim3 grid((unsigned)(p.n_segments * p.n_split_max * p.hkv));
     switch (head_dim) {
     case 64:
         return launch_kind<64>(p, kind, qt, grid, st);
