@@ -142,6 +142,16 @@ __device__ __forceinline__ void merge_scales(float m, float mb, float &mn, float
     fb = exp2_fast(mb - ms);
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences
+// global memory, which waits for every load and store the wave has in
+// flight (a full HBM round trip for the stores just issued).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ void report(int32_t *err, int bits)
 {
     if (err != nullptr && bits != 0)

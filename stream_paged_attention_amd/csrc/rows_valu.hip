@@ -478,9 +478,10 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
         // come first in key order and run through a rolling pipeline: CH
         // tiles are in flight, and as soon as tile i is folded its registers
         // take the loads of tile i + CH.  Loads past the last full tile
-        // repeat it (an L2 hit, not HBM traffic) so that every wait before a
-        // fold is an exact count in issue order.  The masked tail (split
-        // end, causal rows) is folded one tile at a time by its own loop.
+        // repeat it (an L2 hit, never waited for: the barriers below order
+        // LDS only) so that every wait before a fold is an exact count in
+        // issue order.  The masked tail (split end, causal rows) is folded
+        // one tile at a time by its own loop.
         const int n_full = max(0, min(n_tiles, (lim_min - k0) / TK));
         const int my_full = n_full > wave ? (n_full - wave + kWaves - 1) / kWaves : 0;
         for (int b0 = 0; b0 < my_full; b0 += 64) {
@@ -557,7 +558,7 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
             if (lane == 0)
                 xm[wave][v] = st.m[v];
         }
-        __syncthreads();
+        lds_barrier();
         for (int e = threadIdx.x; e < QT * (D / 2); e += kThreads) {
             const int v = e / (D / 2);
             const int d = 2 * (e % (D / 2));
@@ -606,7 +607,7 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
                     b0 | (b1 << 16);
             }
         }
-        __syncthreads();
+        lds_barrier();   // xo, xl and xm are rewritten by the next pass
     }
     if (threadIdx.x == 0 && g == 0 && t == 0)
         report(p.err, errbits);
