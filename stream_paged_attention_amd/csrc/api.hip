@@ -11,6 +11,8 @@
 
 namespace tfa {
 hipError_t launch_rows_valu(const RowsParams &p, int head_dim, int kind, int qt, hipStream_t st);
+hipError_t launch_rows_mfma(const RowsParams &p, int head_dim, int kind, int max_q, hipStream_t st);
+int mfma_query_tile(int head_dim);
 hipError_t launch_merge(const RowsParams &p, int head_dim, int max_rows, hipStream_t st);
 hipError_t launch_argmax(const uint16_t *logits, int n_rows, int vocab, int64_t row_stride,
                          int32_t *ids, uint8_t *flags, void *workspace, hipStream_t st);
@@ -96,6 +98,7 @@ tfa::RowsParams make_params(const tf_attn_args *a)
     p.split_keys = a->split_keys;
     p.n_split_max = n_splits_of(a->max_keys, a->split_keys);
     p.c_log2 = (float)((double)a->scale * 1.4426950408889634073599);
+    p.mfma_min_q = tfa::kMfmaMinQ;
     return p;
 }
 
@@ -214,10 +217,20 @@ int tf_attn_rows(const tf_attn_args *a, hipStream_t stream)
     // one block per (split, segment, kv head), in a one-dimensional grid
     if ((int64_t)p.n_split_max * p.n_segments * p.hkv > (int64_t)INT32_MAX / 256)
         return TF_E_UNSUPPORTED;
-    const int nq_max = a->max_rows * p.group;
+    // Segments with at most kMfmaMinQ query vectors per kv head (decode,
+    // short verify) run on the VALU kernel, the others on the MFMA kernel;
+    // the choice depends on the segment alone.
+    const int64_t nq_max = (int64_t)a->max_rows * p.group;
     const int qt = nq_max <= 4 ? 4 : 8;
     if (tfa::launch_rows_valu(p, a->head_dim, a->kind, qt, stream) != hipSuccess)
         return TF_E_LAUNCH;
+    if (nq_max > p.mfma_min_q) {
+        const int n_qt = (int)((nq_max + tfa::mfma_query_tile(a->head_dim) - 1) / tfa::mfma_query_tile(a->head_dim));
+        if ((int64_t)n_qt * p.n_split_max * p.n_segments * p.hkv > (int64_t)INT32_MAX / 512)
+            return TF_E_UNSUPPORTED;
+        if (tfa::launch_rows_mfma(p, a->head_dim, a->kind, (int)nq_max, stream) != hipSuccess)
+            return TF_E_LAUNCH;
+    }
     return TF_OK;
 }
 

@@ -33,7 +33,13 @@ struct RowsParams {
     int split_keys;        // 0 = one split per (row, head), written straight to out
     int n_split_max;       // grid extent per segment
     float c_log2;          // scale * log2(e): scores are kept in base-2 units
+    int mfma_min_q;        // segments with more query vectors per kv head than this
+                           // (n_rows * group) take the matrix-core kernel
 };
+
+// Query vectors per kv head above which a segment is served by the MFMA
+// kernel (prompt chunks, long verify rounds); at or below, by the VALU kernel.
+constexpr int kMfmaMinQ = 8;
 
 // Loads through the global address space.  Pointers that come out of the
 // segment table are generic; read through them directly the compiler emits

@@ -1,0 +1,620 @@
+// tf_attn_rows, matrix-core path: segments with many query vectors per kv
+// head (prompt chunks, long verify rounds), with bf16 MFMA for the score and
+// value products (TensorFold PR #1503, the paged prompt kernels with the
+// dense tiles on the tensor cores; PR #1653, the head-dim-256 paged prompt
+// kernels with the page id hoisted per tile).
+//
+// Work item = one workgroup = (segment, kv head g, split t, query tile).  A
+// query tile is QB query vectors (row-major over the segment's rows, the
+// group's query heads fastest); each of the NW waves owns NQB blocks of 16.
+//
+// Per 32-key tile, all from LDS, each wave computes
+//     S^T = K Q^T          (v_mfma_f32_16x16x32_bf16, A = K rows, B = Q^T)
+// so that a lane holds the scores of one query vector (lane % 16) for four
+// keys of each 16-key block, then the online softmax for its query vector,
+// and
+//     O^T += V^T P^T       (A = V^T from ds_read_tr16_b64, B = P^T in bf16)
+// where P^T is exactly the S^T register layout: no lane exchange between
+// the two products.  P is carried as two bf16 terms (its rounding and the
+// remainder), each multiplied in, so the weights keep ~16 bits.  Products
+// against a block of ones accumulate l = sum p (the same two terms) next
+// to O.
+//
+// K/V tiles are staged through LDS by direct global->LDS loads (16 bytes a
+// lane, 1 KB a wave instruction), double buffered: the next tile's loads are
+// in flight while the current one is multiplied.  Within a key row the
+// 16-byte units are XOR-swizzled by the key index so that the 16 lanes
+// reading one unit column hit distinct banks.  Three tile buffers: two
+// tiles in flight while the third is multiplied, one barrier per tile.
+//
+// Masking (causal rows, split end, keys past the count) happens on the
+// scores.  A masked key's value must add exactly nothing, but 0 * NaN = NaN
+// on the matrix core: in tiles that mask anything, nonfinite value elements
+// are replaced by 0 before the product, and an indicator product records
+// which (dimension, query vector) outputs saw a nonfinite value among their
+// visible keys; those are written as NaN (the NaN rule for values).
+#include "device.hpp"
+
+namespace tfa {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kKT = 32;                // keys per tile
+constexpr int kNBuf = 3;               // LDS tile buffers: two tiles in flight, one in use
+constexpr float kMLazy = 8.0f;         // log2 of the largest weight a stale reference may give
+
+template <int D>
+struct MGeo {
+    static constexpr int NW = D == 64 ? 4 : 8;        // waves per workgroup
+    static constexpr int KS = D / 32;                 // 32-dim steps of the score product
+    static constexpr int DB = D / 16;                 // 16-dim blocks of the output
+    static constexpr int UPR = D / 8;                 // 16-byte units per key row
+    static constexpr int NQB = D == 256 ? 1 : 2;      // 16-vector blocks per wave
+    static constexpr int QB = NW * 16 * NQB;          // query vectors per workgroup
+    static constexpr int TILE = kKT * D * 2;          // bytes of one K (or V) tile
+    static constexpr int LOADS = TILE / 1024 / NW;    // 1 KB wave loads per wave per tile (K or V)
+    static_assert(LOADS >= 1 && LOADS * NW * 1024 == TILE, "tile must split into 1 KB wave loads");
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
+{
+    // v_cvt_pk_bf16_f32: round to nearest even
+    typedef __bf16 bf16x2_t2 __attribute__((ext_vector_type(2)));
+    bf16x2_t2 v;
+    v.x = (__bf16)a;
+    v.y = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Byte offset of 16-byte unit `c` of key row `key` in an LDS tile.
+template <int D>
+__device__ __forceinline__ uint32_t unit_off(int key, int c)
+{
+    using G = MGeo<D>;
+    return (uint32_t)(key * G::UPR + (c ^ (key & (G::UPR - 1)))) * 16u;
+}
+
+// Workgroup barrier with no fence.  The LDS tiles are written by direct
+// global->LDS loads; each wave establishes their completion itself with an
+// explicit vmcnt wait before the barrier (a fence would also wait for the
+// tiles still in flight).  The memory clobber keeps the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void tile_barrier()
+{
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// One direct global->LDS load: 16 bytes per lane from `src` into LDS at
+// lds_base + 16 * lane (lds_base is wave-uniform, in M0).  Issued from asm
+// so that the compiler does not count it against the LDS reads of the tile
+// being multiplied (it would wait for every tile in flight before each);
+// the kernel waits for these loads explicitly.  No register is written.
+// M0 is written here and nowhere else in this file's kernels (the compiler
+// sets it only for LDS-DMA builtins, which are not used): tests check the
+// generated code for any other M0 access.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_base), "v"(src)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(n), n = 0 .. 63 (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int D, int KIND>
+__global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams p)
+{
+    using G = MGeo<D>;
+    constexpr int KS = G::KS, DB = G::DB, NQB = G::NQB, QB = G::QB, LOADS = G::LOADS, NW = G::NW;
+    __shared__ __attribute__((aligned(1024))) char kv_lds[kNBuf][2][G::TILE];   // [buffer][K, V]
+
+    // ---- work item: kv head fastest, then segment, split, query tile
+    // slowest, so that the query tiles of one (kv head, split) land on one
+    // XCD (round-robin dispatch) and share its L2
+    int rest = blockIdx.x;
+    const int g = rest % p.hkv;
+    rest /= p.hkv;
+    const int seg_i = rest % p.n_segments;
+    rest /= p.n_segments;
+    const int t = rest % p.n_split_max;
+    const int qt = rest / p.n_split_max;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lg = lane >> 4;     // lane group (0..3)
+    const int lc = lane & 15;     // lane column
+
+    const tf_segment &sd = p.segs[seg_i];
+    const char *kbase = static_cast<const char *>(sd.k);
+    const char *vbase = static_cast<const char *>(sd.v);
+    const int32_t *pages = sd.pages;
+    const int capacity = sd.capacity, first = sd.first, row_offset = sd.row_offset;
+    const int n_rows = sd.n_rows, kc = sd.key_count, partial_offset = sd.partial_offset;
+
+    const int group = p.group;
+    const int nq = n_rows * group;
+    // rows_valu_kernel serves the segments with few query vectors
+    if (nq <= p.mfma_min_q)
+        return;
+    const bool rows_ok = n_rows >= 1 && n_rows <= kc && row_offset >= 0 &&
+                         (int64_t)row_offset + n_rows <= p.total_rows;
+    if (!rows_ok) {
+        if (threadIdx.x == 0 && g == 0 && t == 0 && qt == 0)
+            report(p.err, TF_ERR_BAD_ROWS);
+        return;
+    }
+    if (qt * QB >= nq)
+        return;
+    int errbits = 0;
+    if constexpr (KIND == TF_KV_PAGED) {
+        if (pages == nullptr || capacity < 0 || (int64_t)kc > ((int64_t)capacity << p.page_shift))
+            errbits |= TF_ERR_PAST_PAGES;
+    } else {
+        if (kc > capacity)
+            errbits |= TF_ERR_PAST_PAGES;
+    }
+    if constexpr (KIND == TF_KV_RING) {
+        if (first < 0 || first >= capacity)
+            errbits |= TF_ERR_BAD_RING;
+    }
+    const int n_splits = p.split_keys > 0 ? (kc + p.split_keys - 1) / p.split_keys : 1;
+    if (t >= n_splits)
+        return;
+    bool parts_ok = true;
+    if (p.split_keys > 0) {
+        const int64_t need = (int64_t)n_rows * p.hq * n_splits;
+        parts_ok = partial_offset >= 0 && (int64_t)partial_offset + need <= p.max_records;
+        if (!parts_ok)
+            errbits |= TF_ERR_PARTIALS;
+    }
+    const int k0 = p.split_keys > 0 ? t * p.split_keys : 0;
+    const int k_end = p.split_keys > 0 ? min(k0 + p.split_keys, kc) : kc;
+    const float c = p.c_log2;
+    const float lazy = kMLazy / c;
+
+    // ---- this lane's query vectors (one per 16-vector block) and limits
+    const int qv0 = qt * QB + wave * (16 * NQB);
+    int lim[NQB];
+    bool qvalid[NQB];
+    int lim_min = INT32_MAX, lim_max = k0;
+#pragma unroll
+    for (int b = 0; b < NQB; ++b) {
+        const int qv = qv0 + b * 16 + lc;
+        qvalid[b] = qv < nq;
+        const int r = qv / group;
+        lim[b] = qvalid[b] ? min(kc - n_rows + r + 1, k_end) : 0;
+    }
+    // wave-wide visible range: tiles below lim_min are unmasked for every
+    // query vector of the wave, tiles at or past lim_max are invisible
+#pragma unroll
+    for (int b = 0; b < NQB; ++b) {
+        int lo_b = qvalid[b] ? lim[b] : INT32_MAX;
+        int hi_b = qvalid[b] ? lim[b] : k0;
+        // reduce over the 64 lanes (the 4 lane groups hold the same values)
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            lo_b = min(lo_b, __shfl_xor(lo_b, off));
+            hi_b = max(hi_b, __shfl_xor(hi_b, off));
+        }
+        lim_min = min(lim_min, __builtin_amdgcn_readfirstlane(lo_b));
+        lim_max = max(lim_max, __builtin_amdgcn_readfirstlane(hi_b));
+    }
+    // workgroup-wide number of tiles: every wave loads its share of every
+    // tile the workgroup needs
+    __shared__ int wg_hi[NW];
+    if (lane == 0)
+        wg_hi[wave] = lim_max;
+    lds_barrier();
+    int blk_hi = k0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        blk_hi = max(blk_hi, wg_hi[w]);
+    const int n_tiles = errbits ? 0 : (blk_hi - k0 + kKT - 1) / kKT;
+    const bool wave_live = lim_max > k0;   // this wave has a visible key in the split
+
+    // ---- Q^T fragments (B operand): vector lc of block b, dims 32s + 8 lg .. + 8
+    u32x4_t qf[NQB][KS];
+#pragma unroll
+    for (int b = 0; b < NQB; ++b) {
+        const int qv = qv0 + b * 16 + lc;
+        const int r = qv / group;
+        const int h = g * group + qv % group;
+        const char *qrow = reinterpret_cast<const char *>(p.q) +
+                           ((size_t)(row_offset + (qvalid[b] ? r : 0)) * p.hq + h) * (D * 2);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            qf[b][s] = qvalid[b] ? load_global<u32x4_t>(qrow + (s * 32 + lg * 8) * 2) : u32x4_t{0, 0, 0, 0};
+        }
+    }
+
+    // ---- K/V tile loads: wave `wave` fills 1 KB chunks wave*LOADS .. +LOADS
+    // of each tile; lane `lane` of chunk ch fills unit U = ch*64 + lane
+    bool page_bad = false;
+    int pid = 0;
+    auto load_pids = [&](int i0) {
+        if constexpr (KIND == TF_KV_PAGED) {
+            const int ti = i0 + lane;
+            pid = ti < n_tiles ? load_global<int32_t>(pages + ((k0 + ti * kKT) >> p.page_shift)) : 0;
+        }
+    };
+    auto issue = [&](int i, int buf) {
+        const int kt = k0 + i * kKT;
+        const char *kb_ = kbase;
+        const char *vb_ = vbase;
+        size_t run = 0;
+        if constexpr (KIND == TF_KV_PAGED) {
+            int page = __builtin_amdgcn_readlane(pid, i & 63);
+            if ((unsigned)page >= (unsigned)p.pool_pages) {
+                page_bad = true;
+                page = 0;
+            }
+            run = (((size_t)page * p.hkv + g) * p.page_size + (kt & (p.page_size - 1))) * (D * 2);
+        } else {
+            run = (size_t)g * capacity * (D * 2);
+        }
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+            const int ch = wave * LOADS + u;
+            const int U = ch * 64 + lane;
+            const int key = U / G::UPR;
+            const int cu = (U % G::UPR) ^ (key & (G::UPR - 1));
+            size_t off;
+            if constexpr (KIND == TF_KV_PAGED) {
+                off = run + (size_t)key * (D * 2) + cu * 16;
+            } else {
+                // clamp keys past the count to the last key (in bounds; masked)
+                int j = min(kt + key, kc - 1);
+                if constexpr (KIND == TF_KV_RING) {
+                    j += first;
+                    j -= (j >= capacity) ? capacity : 0;
+                }
+                off = run + (size_t)j * (D * 2) + cu * 16;
+            }
+            // LDS byte addresses of the two destination chunks
+            const uint32_t lk = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char *)(
+                &kv_lds[buf][0][ch * 1024]));
+            const uint32_t lv = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char *)(
+                &kv_lds[buf][1][ch * 1024]));
+            dma16(kb_ + off, __builtin_amdgcn_readfirstlane(lk));
+            dma16(vb_ + off, __builtin_amdgcn_readfirstlane(lv));
+        }
+    };
+
+    // ---- state per block of 16 query vectors (per lane: its vector)
+    float m[NQB], mc[NQB], thr[NQB], lo[NQB];
+    f32x4_t o[NQB][DB];
+    f32x4_t lsum[NQB];   // ones-block product: every element is l of the lane's vector
+    uint32_t nanmask[NQB][(DB * 4 + 31) / 32];
+#pragma unroll
+    for (int b = 0; b < NQB; ++b) {
+        m[b] = -INFINITY;
+        mc[b] = 0.0f;
+        thr[b] = -INFINITY;
+        lo[b] = INFINITY;
+        lsum[b] = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int d = 0; d < DB; ++d)
+            o[b][d] = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int w = 0; w < (DB * 4 + 31) / 32; ++w)
+            nanmask[b][w] = 0;
+    }
+    const uint32_t one2 = 0x3F803F80u;   // two bf16 ones
+    const bf16x8_t ones = as_bf16x8(u32x4_t{one2, one2, one2, one2});
+
+    // Q fragments and the first page ids complete before the pipeline
+    // starts: a register load still pending inside the loop would make every
+    // iteration wait for all loads (the tile loads issued from asm included)
+    if (n_tiles > 0)
+        load_pids(0);
+    wait_vm<0>();
+    if (n_tiles > 0) {
+        issue(0, 0);
+        if (n_tiles > 1)
+            issue(1, 1);
+    }
+    for (int i = 0; i < n_tiles; ++i) {
+        const int buf = i % kNBuf;
+        const int kt = k0 + i * kKT;
+        // tile i's loads are the older of the (at most) two tiles in flight;
+        // the LDS reads of tile i - 1 are complete (their products consumed
+        // them) before this wave reaches the barrier
+        if (i + 1 < n_tiles)
+            wait_vm<2 * LOADS>();
+        else
+            wait_vm<0>();
+        // after the barrier: every wave's loads of tile i have landed and
+        // every wave is done with tile i - 1, whose buffer takes tile i + 2
+        tile_barrier();
+        if (i + 2 < n_tiles) {
+            if (((i + 2) & 63) == 0) {
+                // next batch of page ids (every 64 tiles): drains the tiles in flight
+                load_pids(i + 2);
+                wait_vm<0>();
+            }
+            issue(i + 2, (i + 2) % kNBuf);
+        }
+        if (!wave_live || kt >= lim_max)
+            continue;    // nothing visible to this wave in the tile
+        const char *kt_lds = kv_lds[buf][0];
+        const char *vt_lds = kv_lds[buf][1];
+        const bool full = kt + kKT <= lim_min;
+
+        // -- scores S^T: 2 key blocks x NQB vector blocks
+        f32x4_t s[NQB][2];
+#pragma unroll
+        for (int b = 0; b < NQB; ++b)
+            s[b][0] = s[b][1] = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(
+                    kt_lds + unit_off<D>(kb * 16 + lc, ks * 4 + lg));
+#pragma unroll
+                for (int b = 0; b < NQB; ++b)
+                    s[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[b][ks]),
+                                                                      s[b][kb], 0, 0, 0);
+            }
+        }
+
+        // -- online softmax per vector; P^T fragments in bf16
+        u32x4_t pf[NQB], pl[NQB];   // P^T in bf16: rounded value and its remainder
+        uint64_t need = 0;
+        float tmax[NQB];
+#pragma unroll
+        for (int b = 0; b < NQB; ++b) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float x = s[b][kb][e];
+                    if (!full) {
+                        const int key = kt + kb * 16 + lg * 4 + e;
+                        const bool vis = key < lim[b];
+                        lo[b] = min2(lo[b], vis ? x : INFINITY);
+                        x = vis ? x : -INFINITY;
+                        s[b][kb][e] = x;
+                    } else {
+                        lo[b] = min2(lo[b], x);
+                    }
+                    mx = max2(mx, x);
+                }
+            }
+            float a, bb;
+            swap16(mx, a, bb);
+            mx = max2(a, bb);
+            swap32(mx, a, bb);
+            mx = max2(a, bb);
+            tmax[b] = mx;
+            need |= __builtin_amdgcn_ballot_w64(mx > thr[b]);
+        }
+        if (need != 0) {
+#pragma unroll
+            for (int b = 0; b < NQB; ++b) {
+                const bool up = tmax[b] > m[b];
+                const float alpha = up ? exp2_fast((m[b] - tmax[b]) * c) : 1.0f;
+                m[b] = up ? tmax[b] : m[b];
+                mc[b] = up ? tmax[b] * c : mc[b];
+                thr[b] = up ? tmax[b] + lazy : thr[b];
+                lsum[b] *= alpha;
+#pragma unroll
+                for (int d = 0; d < DB; ++d)
+                    o[b][d] *= alpha;
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NQB; ++b) {
+            float pe[8];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    pe[kb * 4 + e] = exp2_fast(fmaf(s[b][kb][e], c, -mc[b]));
+            // p = hi + lo, both bf16: the value product takes the two parts, so
+            // the weights keep about 16 significant bits instead of 8
+            float pr[8];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                pf[b][w] = pack_bf16(pe[2 * w], pe[2 * w + 1]);
+                pr[2 * w] = pe[2 * w] - bf16_lo(pf[b][w]);
+                pr[2 * w + 1] = pe[2 * w + 1] - bf16_hi(pf[b][w]);
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                pl[b][w] = pack_bf16(pr[2 * w], pr[2 * w + 1]);
+            lsum[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, as_bf16x8(pf[b]), lsum[b], 0, 0, 0);
+            lsum[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, as_bf16x8(pl[b]), lsum[b], 0, 0, 0);
+        }
+
+        // -- values: O^T += V^T P^T per 16-dim block.  V^T fragment of lane
+        // (lg, lc): dims 16 db + lc, keys 4 lg .. + 4 and 16 + 4 lg .. + 4,
+        // by two transposed reads of 4 x 16 blocks
+        uint64_t bad = 0;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            i16x4_t h0, h1;
+            {
+                // the 16 lanes of group lg read the 4 x 16 block of keys
+                // 4 lg .. + 4 (resp. 16 + 4 lg ..), dims 16 db .. + 16: lane
+                // i of the group reads key 4 lg + i / 4, dims 16 db + 4 (i % 4) .. + 4
+                const int key0 = lg * 4 + (lc >> 2);
+                const int dim = db * 16 + (lc & 3) * 4;
+                const uint32_t o0 = unit_off<D>(key0, dim >> 3) + (dim & 7) * 2;
+                const uint32_t o1 = unit_off<D>(key0 + 16, dim >> 3) + (dim & 7) * 2;
+                h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(vt_lds + o0));
+                h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(vt_lds + o1));
+            }
+            u32x4_t vf = u32x4_t{(uint32_t)(uint16_t)h0[0] | ((uint32_t)(uint16_t)h0[1] << 16),
+                                 (uint32_t)(uint16_t)h0[2] | ((uint32_t)(uint16_t)h0[3] << 16),
+                                 (uint32_t)(uint16_t)h1[0] | ((uint32_t)(uint16_t)h1[1] << 16),
+                                 (uint32_t)(uint16_t)h1[2] | ((uint32_t)(uint16_t)h1[3] << 16)};
+            if (!full) {
+                // nonfinite values become 0 (exponent all ones -> zero); the
+                // indicator keeps which dims had one, per key slot
+                u32x4_t ind;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t x = vf[w];
+                    const bool nlo = (x & 0x7F80u) == 0x7F80u;
+                    const bool nhi = (x & 0x7F800000u) == 0x7F800000u;
+                    vf[w] = (nlo ? 0u : (x & 0xFFFFu)) | (nhi ? 0u : (x & 0xFFFF0000u));
+                    ind[w] = (nlo ? 0x3F80u : 0u) | (nhi ? 0x3F800000u : 0u);
+                    bad |= __builtin_amdgcn_ballot_w64(nlo || nhi);
+                }
+                if (bad != 0) {
+                    // count of visible nonfinite values per (dim, vector)
+#pragma unroll
+                    for (int b = 0; b < NQB; ++b) {
+                        u32x4_t visf;
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            const int ka = kt + (w >> 1) * 16 + lg * 4 + (w & 1) * 2;
+                            visf[w] = (ka < lim[b] ? 0x3F80u : 0u) | (ka + 1 < lim[b] ? 0x3F800000u : 0u);
+                        }
+                        const f32x4_t cnt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            as_bf16x8(ind), as_bf16x8(visf), f32x4_t{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int bit = db * 4 + e;
+                            if (cnt[e] > 0.0f)
+                                nanmask[b][bit >> 5] |= 1u << (bit & 31);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < NQB; ++b) {
+                o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), as_bf16x8(pf[b]), o[b][db],
+                                                                   0, 0, 0);
+                o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), as_bf16x8(pl[b]), o[b][db],
+                                                                   0, 0, 0);
+            }
+        }
+    }
+    if (page_bad) {
+        report(p.err, TF_ERR_BAD_PAGE);
+#pragma unroll
+        for (int b = 0; b < NQB; ++b)
+            lsum[b] = f32x4_t{NAN, NAN, NAN, NAN};
+    }
+
+    // ---- write: lane (lg, lc) holds dims 16 db + 4 lg .. + 4 of vector lc
+#pragma unroll
+    for (int b = 0; b < NQB; ++b) {
+        float a, bb;
+        swap16(lo[b], a, bb);
+        float lw = min2(a, bb);
+        swap32(lw, a, bb);
+        lw = min2(a, bb);
+        if (!qvalid[b])
+            continue;
+        const int qv = qv0 + b * 16 + lc;
+        const int r = qv / group;
+        const int h = g * group + qv % group;
+        const float ll = lsum[b][0];
+        const bool nan_out = __builtin_isnan(ll) || lw == -INFINITY || errbits != 0;
+        if (p.split_keys > 0) {
+            if (!parts_ok)
+                continue;
+            const int64_t recno = partial_offset + ((int64_t)r * p.hq + h) * n_splits + t;
+            float *rec = p.partials + recno * (D + 4);
+            if (lg == 0)
+                *reinterpret_cast<float4 *>(rec) =
+                    make_float4(nan_out ? NAN : m[b] * (c * kLn2), nan_out ? NAN : ll, 0.0f, 0.0f);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                float4 v;
+                float *vp = &v.x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int bit = db * 4 + e;
+                    const bool nb = (nanmask[b][bit >> 5] >> (bit & 31)) & 1u;
+                    vp[e] = (nan_out || nb) ? NAN : o[b][db][e];
+                }
+                *reinterpret_cast<float4 *>(rec + 4 + db * 16 + lg * 4) = v;
+            }
+        } else {
+            uint16_t *dst = p.out + ((size_t)(row_offset + r) * p.hq + h) * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                uint16_t hb[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int bit = db * 4 + e;
+                    const bool nb = (nanmask[b][bit >> 5] >> (bit & 31)) & 1u;
+                    hb[e] = (nan_out || nb) ? kBf16NaN : bf16_out(o[b][db][e] / ll);
+                }
+                *reinterpret_cast<uint2 *>(dst + db * 16 + lg * 4) =
+                    make_uint2((uint32_t)hb[0] | ((uint32_t)hb[1] << 16), (uint32_t)hb[2] | ((uint32_t)hb[3] << 16));
+            }
+        }
+    }
+    if (threadIdx.x == 0 && g == 0 && t == 0 && qt == 0)
+        report(p.err, errbits);
+}
+
+template <int D>
+hipError_t launch_kind_m(const RowsParams &p, int kind, int n_qt, hipStream_t st)
+{
+    const dim3 grid((unsigned)(n_qt * p.n_split_max * p.n_segments * p.hkv));
+    const dim3 block(64 * MGeo<D>::NW);
+    switch (kind) {
+    case TF_KV_CONTIG:
+        hipLaunchKernelGGL((rows_mfma_kernel<D, TF_KV_CONTIG>), grid, block, 0, st, p);
+        break;
+    case TF_KV_PAGED:
+        hipLaunchKernelGGL((rows_mfma_kernel<D, TF_KV_PAGED>), grid, block, 0, st, p);
+        break;
+    default:
+        hipLaunchKernelGGL((rows_mfma_kernel<D, TF_KV_RING>), grid, block, 0, st, p);
+        break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Query vectors per MFMA workgroup for head dim D.
+int mfma_query_tile(int head_dim)
+{
+    return head_dim == 256 ? MGeo<256>::QB : (head_dim == 128 ? MGeo<128>::QB : MGeo<64>::QB);
+}
+
+// Launch the MFMA rows kernel for the segments with more than p.mfma_min_q
+// query vectors per kv head (max_q bounds them all); one block per (query
+// tile, split, segment, kv head).
+hipError_t launch_rows_mfma(const RowsParams &p, int head_dim, int kind, int max_q, hipStream_t st)
+{
+    const int qb = mfma_query_tile(head_dim);
+    const int n_qt = (max_q + qb - 1) / qb;
+    switch (head_dim) {
+    case 64:
+        return launch_kind_m<64>(p, kind, n_qt, st);
+    case 128:
+        return launch_kind_m<128>(p, kind, n_qt, st);
+    default:
+        return launch_kind_m<256>(p, kind, n_qt, st);
+    }
+}
+
+}  // namespace tfa

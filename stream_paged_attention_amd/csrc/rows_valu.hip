@@ -340,6 +340,10 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
     s.key_count = sd.key_count;
     s.partial_offset = sd.partial_offset;
 
+    // segments with many query vectors per kv head go to rows_mfma_kernel
+    if (s.n_rows * p.group > p.mfma_min_q)
+        return;
+
     // ---- per-segment checks (identical in every work item of the segment)
     const bool rows_ok = s.n_rows >= 1 && s.n_rows <= s.key_count && s.row_offset >= 0 &&
                          (int64_t)s.row_offset + s.n_rows <= p.total_rows;
