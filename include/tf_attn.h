@@ -131,6 +131,9 @@ typedef struct tf_attn_args {
     int32_t total_rows;       /* packed query rows of q and out                              */
     int32_t max_rows;         /* >= every segment's n_rows (grid sizing only)                */
     int32_t max_keys;         /* >= every segment's key_count (grid sizing only)             */
+    int32_t min_rows;         /* <= every segment's n_rows, or 0 if unknown (kernel choice
+                                 only: lets a launch whose segments all have many query
+                                 vectors skip the decode kernel)                             */
     int32_t n_q_heads;        /* Hq                                                          */
     int32_t n_kv_heads;       /* Hkv; query head h reads kv head h / (Hq / Hkv)              */
     int32_t head_dim;         /* 64, 128 or 256                                              */

@@ -43,7 +43,8 @@ class tf_segment(ctypes.Structure):
 class tf_attn_args(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("n_segments", ctypes.c_int32),
                 ("total_rows", ctypes.c_int32), ("max_rows", ctypes.c_int32),
-                ("max_keys", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("max_keys", ctypes.c_int32), ("min_rows", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("pool_pages", ctypes.c_int32),
                 ("split_keys", ctypes.c_int32), ("scale", ctypes.c_float),

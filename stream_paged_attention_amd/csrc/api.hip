@@ -37,7 +37,8 @@ int check_args(const tf_attn_args *a, bool need_partials)
         return TF_E_INVALID;
     if (a->kind != TF_KV_CONTIG && a->kind != TF_KV_PAGED && a->kind != TF_KV_RING)
         return TF_E_INVALID;
-    if (a->n_segments < 0 || a->total_rows < 0 || a->max_rows < 0 || a->max_keys < 0)
+    if (a->n_segments < 0 || a->total_rows < 0 || a->max_rows < 0 || a->max_keys < 0 ||
+        a->min_rows < 0 || a->min_rows > a->max_rows)
         return TF_E_INVALID;
     if (a->n_q_heads < 1 || a->n_kv_heads < 1 || a->n_q_heads % a->n_kv_heads != 0)
         return TF_E_INVALID;
@@ -168,7 +169,7 @@ int tf_check_segments(const tf_attn_args *a, const tf_segment *host_segs)
         const tf_segment &s = host_segs[i];
         if (s.k == nullptr || s.v == nullptr || !aligned16(s.k) || !aligned16(s.v))
             return TF_E_INVALID;
-        if (s.n_rows < 1 || s.n_rows > s.key_count || s.n_rows > a->max_rows ||
+        if (s.n_rows < 1 || s.n_rows > s.key_count || s.n_rows > a->max_rows || s.n_rows < a->min_rows ||
             s.key_count > a->max_keys)
             return TF_E_INVALID;
         if (s.row_offset < 0 || (int64_t)s.row_offset + s.n_rows > a->total_rows)
@@ -213,7 +214,7 @@ int tf_attn_rows(const tf_attn_args *a, hipStream_t stream)
         return rc;
     if (a->n_segments == 0)
         return TF_OK;
-    const tfa::RowsParams p = make_params(a);
+    tfa::RowsParams p = make_params(a);
     // one block per (split, segment, kv head), in a one-dimensional grid
     if ((int64_t)p.n_split_max * p.n_segments * p.hkv > (int64_t)INT32_MAX / 256)
         return TF_E_UNSUPPORTED;
@@ -222,8 +223,14 @@ int tf_attn_rows(const tf_attn_args *a, hipStream_t stream)
     // the choice depends on the segment alone.
     const int64_t nq_max = (int64_t)a->max_rows * p.group;
     const int qt = nq_max <= 4 ? 4 : 8;
-    if (tfa::launch_rows_valu(p, a->head_dim, a->kind, qt, stream) != hipSuccess)
+    if (a->min_rows > 0 && (int64_t)a->min_rows * p.group > p.mfma_min_q) {
+        // every segment has many query vectors: no decode launch, and the
+        // matrix-core kernel takes all segments (so none is dropped even if
+        // the hint were wrong)
+        p.mfma_min_q = 0;
+    } else if (tfa::launch_rows_valu(p, a->head_dim, a->kind, qt, stream) != hipSuccess) {
         return TF_E_LAUNCH;
+    }
     if (nq_max > p.mfma_min_q) {
         const int n_qt = (int)((nq_max + tfa::mfma_query_tile(a->head_dim) - 1) / tfa::mfma_query_tile(a->head_dim));
         if ((int64_t)n_qt * p.n_split_max * p.n_segments * p.hkv > (int64_t)INT32_MAX / 512)

@@ -39,7 +39,7 @@ struct RowsParams {
 
 // Query vectors per kv head above which a segment is served by the MFMA
 // kernel (prompt chunks, long verify rounds); at or below, by the VALU kernel.
-constexpr int kMfmaMinQ = 8;
+constexpr int kMfmaMinQ = 4;
 
 // Loads through the global address space.  Pointers that come out of the
 // segment table are generic; read through them directly the compiler emits

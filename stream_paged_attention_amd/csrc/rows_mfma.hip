@@ -24,8 +24,8 @@
 // lane, 1 KB a wave instruction), double buffered: the next tile's loads are
 // in flight while the current one is multiplied.  Within a key row the
 // 16-byte units are XOR-swizzled by the key index so that the 16 lanes
-// reading one unit column hit distinct banks.  Three tile buffers: two
-// tiles in flight while the third is multiplied, one barrier per tile.
+// reading one unit column hit distinct banks.  NBUF tile buffers: NBUF - 1
+// tiles in flight while one is multiplied, one barrier per tile.
 //
 // Masking (causal rows, split end, keys past the count) happens on the
 // scores.  A masked key's value must add exactly nothing, but 0 * NaN = NaN
@@ -44,19 +44,23 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kKT = 32;                // keys per tile
-constexpr int kNBuf = 3;               // LDS tile buffers: two tiles in flight, one in use
 constexpr float kMLazy = 8.0f;         // log2 of the largest weight a stale reference may give
 
 template <int D>
 struct MGeo {
-    static constexpr int NW = D == 64 ? 4 : 8;        // waves per workgroup
+    static constexpr int NW = D == 256 ? 8 : 4;       // waves per workgroup
     static constexpr int KS = D / 32;                 // 32-dim steps of the score product
     static constexpr int DB = D / 16;                 // 16-dim blocks of the output
     static constexpr int UPR = D / 8;                 // 16-byte units per key row
-    static constexpr int NQB = D == 256 ? 1 : 2;      // 16-vector blocks per wave
+    static constexpr int NQB = 1;                     // 16-vector blocks per wave
     static constexpr int QB = NW * 16 * NQB;          // query vectors per workgroup
     static constexpr int TILE = kKT * D * 2;          // bytes of one K (or V) tile
     static constexpr int LOADS = TILE / 1024 / NW;    // 1 KB wave loads per wave per tile (K or V)
+    // LDS tile buffers (K and V): NBUF - 1 tiles in flight while one is
+    // multiplied; 128 KB of LDS at D 256 (one workgroup of 8 waves a CU),
+    // 64 KB below (two workgroups of 4 waves)
+    static constexpr int NBUF = D == 256 ? 4 : (D == 128 ? 4 : 8);
+    static constexpr int PD = NBUF - 1;               // prefetch distance in tiles
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == TILE, "tile must split into 1 KB wave loads");
 };
 
@@ -117,12 +121,28 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until at most `newer` tiles of L loads each are still in flight
+// (newer = 0 .. MAXN, uniform).
+template <int L, int MAXN>
+__device__ __forceinline__ void wait_tiles(int newer)
+{
+    if constexpr (MAXN <= 0) {
+        wait_vm<0>();
+    } else {
+        if (newer >= MAXN)
+            wait_vm<L * MAXN>();
+        else
+            wait_tiles<L, MAXN - 1>(newer);
+    }
+}
+
 template <int D, int KIND>
 __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams p)
 {
     using G = MGeo<D>;
     constexpr int KS = G::KS, DB = G::DB, NQB = G::NQB, QB = G::QB, LOADS = G::LOADS, NW = G::NW;
-    __shared__ __attribute__((aligned(1024))) char kv_lds[kNBuf][2][G::TILE];   // [buffer][K, V]
+    constexpr int NBUF = G::NBUF, PD = G::PD;
+    __shared__ __attribute__((aligned(1024))) char kv_lds[NBUF][2][G::TILE];   // [buffer][K, V]
 
     // ---- work item: kv head fastest, then segment, split, query tile
     // slowest, so that the query tiles of one (kv head, split) land on one
@@ -324,31 +344,28 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
     if (n_tiles > 0)
         load_pids(0);
     wait_vm<0>();
-    if (n_tiles > 0) {
-        issue(0, 0);
-        if (n_tiles > 1)
-            issue(1, 1);
-    }
+#pragma unroll
+    for (int u = 0; u < PD; ++u)
+        if (u < n_tiles)
+            issue(u, u);
     for (int i = 0; i < n_tiles; ++i) {
-        const int buf = i % kNBuf;
+        const int buf = i % NBUF;
         const int kt = k0 + i * kKT;
-        // tile i's loads are the older of the (at most) two tiles in flight;
-        // the LDS reads of tile i - 1 are complete (their products consumed
-        // them) before this wave reaches the barrier
-        if (i + 1 < n_tiles)
-            wait_vm<2 * LOADS>();
-        else
-            wait_vm<0>();
+        // tiles i .. i + PD - 1 are in flight (those that exist); wait for
+        // the oldest.  The LDS reads of tile i - 1 are complete (their
+        // products consumed them) before this wave reaches the barrier.
+        const int newer = min(PD - 1, n_tiles - 1 - i);
+        wait_tiles<2 * LOADS, PD - 1>(newer);
         // after the barrier: every wave's loads of tile i have landed and
-        // every wave is done with tile i - 1, whose buffer takes tile i + 2
+        // every wave is done with tile i - 1, whose buffer takes tile i + PD
         tile_barrier();
-        if (i + 2 < n_tiles) {
-            if (((i + 2) & 63) == 0) {
+        if (i + PD < n_tiles) {
+            if (((i + PD) & 63) == 0) {
                 // next batch of page ids (every 64 tiles): drains the tiles in flight
-                load_pids(i + 2);
+                load_pids(i + PD);
                 wait_vm<0>();
             }
-            issue(i + 2, (i + 2) % kNBuf);
+            issue(i + PD, (i + PD) % NBUF);
         }
         if (!wave_live || kt >= lim_max)
             continue;    // nothing visible to this wave in the tile
@@ -357,21 +374,33 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
         const bool full = kt + kKT <= lim_min;
 
         // -- scores S^T: 2 key blocks x NQB vector blocks
-        f32x4_t s[NQB][2];
+        // (even and odd dim steps accumulate apart: four independent
+        // product chains per vector block keep the matrix pipe busy)
+        f32x4_t s[NQB][2], s2[NQB][2];
 #pragma unroll
         for (int b = 0; b < NQB; ++b)
-            s[b][0] = s[b][1] = f32x4_t{0, 0, 0, 0};
+            s[b][0] = s[b][1] = s2[b][0] = s2[b][1] = f32x4_t{0, 0, 0, 0};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ks += 2) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(
-                    kt_lds + unit_off<D>(kb * 16 + lc, ks * 4 + lg));
+            for (int h = 0; h < 2; ++h) {
 #pragma unroll
-                for (int b = 0; b < NQB; ++b)
-                    s[b][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[b][ks]),
-                                                                      s[b][kb], 0, 0, 0);
+                for (int kb = 0; kb < 2; ++kb) {
+                    const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(
+                        kt_lds + unit_off<D>(kb * 16 + lc, (ks + h) * 4 + lg));
+#pragma unroll
+                    for (int b = 0; b < NQB; ++b) {
+                        f32x4_t &acc = h ? s2[b][kb] : s[b][kb];
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[b][ks + h]),
+                                                                     acc, 0, 0, 0);
+                    }
+                }
             }
+        }
+#pragma unroll
+        for (int b = 0; b < NQB; ++b) {
+            s[b][0] += s2[b][0];
+            s[b][1] += s2[b][1];
         }
 
         // -- online softmax per vector; P^T fragments in bf16
@@ -448,8 +477,7 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
         // (lg, lc): dims 16 db + lc, keys 4 lg .. + 4 and 16 + 4 lg .. + 4,
         // by two transposed reads of 4 x 16 blocks
         uint64_t bad = 0;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
+        auto vfrag = [&](int db) {
             i16x4_t h0, h1;
             {
                 // the 16 lanes of group lg read the 4 x 16 block of keys
@@ -502,12 +530,24 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
                     }
                 }
             }
+            return vf;
+        };
+        // two dim blocks at a time: the rounded and the remainder products
+        // of one block are not back to back (independent chains)
+#pragma unroll
+        for (int db = 0; db < DB; db += 2) {
+            const u32x4_t v0 = vfrag(db), v1 = vfrag(db + 1);
 #pragma unroll
             for (int b = 0; b < NQB; ++b) {
-                o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), as_bf16x8(pf[b]), o[b][db],
-                                                                   0, 0, 0);
-                o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), as_bf16x8(pl[b]), o[b][db],
-                                                                   0, 0, 0);
+                o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v0), as_bf16x8(pf[b]), o[b][db], 0, 0, 0);
+                o[b][db + 1] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v1), as_bf16x8(pf[b]), o[b][db + 1], 0, 0, 0);
+            }
+#pragma unroll
+            for (int b = 0; b < NQB; ++b) {
+                o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v0), as_bf16x8(pl[b]), o[b][db], 0, 0, 0);
+                o[b][db + 1] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v1), as_bf16x8(pl[b]), o[b][db + 1], 0, 0, 0);
             }
         }
     }

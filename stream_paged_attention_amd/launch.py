@@ -118,6 +118,7 @@ class DeviceWorkload:
         a.total_rows = w.total_rows
         a.max_rows = w.max_rows
         a.max_keys = w.max_keys
+        a.min_rows = min((s.n_rows for s in w.segments), default=0)
         a.n_q_heads = w.n_q_heads
         a.n_kv_heads = w.n_kv_heads
         a.head_dim = w.head_dim
@@ -170,6 +171,7 @@ class DeviceWorkload:
             a.total_rows = s.n_rows
             a.max_rows = s.n_rows
             a.max_keys = s.key_count
+            a.min_rows = s.n_rows
             a.q = self.q.data_ptr() + s.row_offset * row_bytes
             a.out = out.data_ptr() + s.row_offset * row_bytes
             part = None

@@ -94,6 +94,7 @@ def _args(**kw):
     a.total_rows = kw.get("total_rows", 2)
     a.max_rows = kw.get("max_rows", 2)
     a.max_keys = kw.get("max_keys", 100)
+    a.min_rows = kw.get("min_rows", 0)
     a.n_q_heads = kw.get("hq", 8)
     a.n_kv_heads = kw.get("hkv", 2)
     a.head_dim = kw.get("d", 128)
@@ -123,6 +124,8 @@ def _args(**kw):
     (dict(max_keys=1, max_rows=2), binding.TF_E_INVALID),
     (dict(pool_pages=0), binding.TF_E_INVALID),
     (dict(split=512), binding.TF_E_WORKSPACE),        # partials missing
+    (dict(min_rows=3, max_rows=2), binding.TF_E_INVALID),
+    (dict(min_rows=-1), binding.TF_E_INVALID),
     (dict(scale=0.0), binding.TF_E_INVALID),
     (dict(scale=-0.1), binding.TF_E_INVALID),
     (dict(scale=float("inf")), binding.TF_E_INVALID),
@@ -162,6 +165,9 @@ def test_check_segments_host_rules():
     assert binding.tf_check_segments(_args(total_rows=3, n_segments=2), overlap) == binding.TF_E_INVALID
     too_many_rows = _host_table([(4, 0, 0, 3, 100)])
     assert binding.tf_check_segments(_args(total_rows=3, max_rows=2), too_many_rows) == binding.TF_E_INVALID
+    # a segment with fewer rows than the min_rows hint
+    assert binding.tf_check_segments(_args(total_rows=3, n_segments=2, min_rows=2), ok) == binding.TF_E_INVALID
+    assert binding.tf_check_segments(_args(total_rows=3, n_segments=2, min_rows=1), ok) == binding.TF_OK
     ring_bad = _host_table([(50, 50, 0, 1, 40)], kind=binding.TF_KV_RING)
     assert binding.tf_check_segments(_args(kind=binding.TF_KV_RING, total_rows=1), ring_bad) == binding.TF_E_INVALID
     ring_past = _host_table([(30, 3, 0, 1, 40)], kind=binding.TF_KV_RING)

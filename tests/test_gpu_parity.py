@@ -170,6 +170,13 @@ SHAPES = [
     ("contig", 128, 16, 2, [3, 1], [777, 64], 96),
     ("ring", 128, 16, 2, [16, 1, 4], [4200, 333, 80], 512),
     ("ring", 256, 8, 2, [2], [129], 64),
+    # more than 8 query vectors per kv head: the matrix-core kernel
+    ("paged", 64, 8, 2, [12], [500], 128),         # D64
+    ("paged", 128, 16, 2, [40, 3], [1100, 90], 256),   # 320 vectors: two query tiles (256 a tile)
+    ("paged", 256, 16, 4, [40], [700], 512),       # 160 vectors: two query tiles (128 a tile)
+    ("paged", 128, 16, 4, [6], [5000], 0),         # one split of 157 tiles: page ids reloaded
+    ("contig", 64, 8, 2, [20], [333], 0),
+    ("ring", 256, 16, 4, [5, 16], [4100, 700], 1024),
 ]
 
 
