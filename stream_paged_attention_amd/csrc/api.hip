@@ -10,7 +10,7 @@
 #include "tf_attn.h"
 
 namespace tfa {
-hipError_t launch_rows_valu(const RowsParams &p, int head_dim, int kind, int qt, hipStream_t st);
+hipError_t launch_rows_valu(const RowsParams &p, int head_dim, int kind, hipStream_t st);
 hipError_t launch_rows_mfma(const RowsParams &p, int head_dim, int kind, int max_q, hipStream_t st);
 int mfma_query_tile(int head_dim);
 hipError_t launch_merge(const RowsParams &p, int head_dim, int max_rows, hipStream_t st);
@@ -222,13 +222,12 @@ int tf_attn_rows(const tf_attn_args *a, hipStream_t stream)
     // short verify) run on the VALU kernel, the others on the MFMA kernel;
     // the choice depends on the segment alone.
     const int64_t nq_max = (int64_t)a->max_rows * p.group;
-    const int qt = nq_max <= 4 ? 4 : 8;
     if (a->min_rows > 0 && (int64_t)a->min_rows * p.group > p.mfma_min_q) {
         // every segment has many query vectors: no decode launch, and the
         // matrix-core kernel takes all segments (so none is dropped even if
         // the hint were wrong)
         p.mfma_min_q = 0;
-    } else if (tfa::launch_rows_valu(p, a->head_dim, a->kind, qt, stream) != hipSuccess) {
+    } else if (tfa::launch_rows_valu(p, a->head_dim, a->kind, stream) != hipSuccess) {
         return TF_E_LAUNCH;
     }
     if (nq_max > p.mfma_min_q) {

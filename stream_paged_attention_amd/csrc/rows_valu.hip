@@ -182,23 +182,33 @@ struct State {
     float o[QT][Geo<D, QT>::DPL];
 };
 
+// max / min as a single v_max_f32 / v_min_f32: the compiler's versions for
+// values of unknown origin add a canonicalising v_max on each input
+__device__ __forceinline__ float vmax(float a, float b)
+{
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float vmin(float a, float b)
+{
+    float r;
+    asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // Combine a value over the key groups of the wave (lanes LPK apart), result
 // in every lane.
-template <int LPK, bool MAX>
-__device__ __forceinline__ float across_groups(float x)
+template <int LPK>
+__device__ __forceinline__ float groups_max(float x)
 {
     float a, b;
     if constexpr (LPK == 8)
-        x = MAX ? max2(x, ror8(x)) : x + ror8(x);
+        x = vmax(x, ror8(x));
     swap16(x, a, b);
-    x = MAX ? max2(a, b) : a + b;
+    x = vmax(a, b);
     swap32(x, a, b);
-    return MAX ? max2(a, b) : a + b;
-}
-template <int LPK>
-__device__ __forceinline__ float groups_min(float x)
-{
-    return -across_groups<LPK, true>(-x);
+    return vmax(a, b);
 }
 
 // Fold one K/V tile.  key0 is the lane's first key.  With MASKED, key
@@ -218,9 +228,12 @@ __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][G
     for (int j = 0; j < NS; ++j) {
 #pragma unroll
         for (int v = 0; v < QT; ++v) {
-            float a = 0.0f;
+            // first product in the three-operand form with an inline 0
+            // (the two-operand form would need a register zeroed first)
+            float a;
+            asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(a) : "v"(qr[v][0]), "v"(kb[j][0]));
 #pragma unroll
-            for (int w = 0; w < W; ++w)
+            for (int w = 1; w < W; ++w)
                 a = dot2_bf16(qr[v][w], kb[j][w], a);
             s[v][j] = group_sum<G::LPK>(a);
         }
@@ -232,12 +245,14 @@ __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][G
     for (int v = 0; v < QT; ++v) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
+            // the smallest counted score: a -inf score gives p = 0, so it
+            // has to be recorded apart (NaN rule)
             if constexpr (MASKED) {
                 const bool vis = key0 + KPS * j < lim[v];
-                st.lo[v] = min2(st.lo[v], vis ? s[v][j] : INFINITY);
+                st.lo[v] = vmin(st.lo[v], vis ? s[v][j] : INFINITY);
                 s[v][j] = vis ? s[v][j] : -INFINITY;
             } else {
-                st.lo[v] = min2(st.lo[v], s[v][j]);
+                st.lo[v] = vmin(st.lo[v], s[v][j]);
             }
             need |= __builtin_amdgcn_ballot_w64(s[v][j] > st.thr[v]);
         }
@@ -249,9 +264,8 @@ __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][G
             float t = s[v][0];
 #pragma unroll
             for (int j = 1; j < NS; ++j)
-                t = max2(t, s[v][j]);
-            t = __builtin_amdgcn_readfirstlane(__float_as_int(across_groups<G::LPK, true>(t)));
-            const float tm = __int_as_float((int)t);
+                t = vmax(t, s[v][j]);
+            const float tm = uniform(groups_max<G::LPK>(t));
             // only a query vector whose own max passed its reference moves;
             // one that saw nothing (all masked) keeps m = -inf and mc = 0
             const bool up = tm > st.m[v];
@@ -383,7 +397,10 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
     const int k_end = p.split_keys > 0 ? min(k0 + p.split_keys, s.key_count) : s.key_count;
     const int n_tiles = errbits ? 0 : (k_end - k0 + TK - 1) / TK;
     const int my_tiles = n_tiles > wave ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
-    const float c = p.c_log2;
+    // the scale lives in a VGPR: the exponent's fma then reads only m * c
+    // from a scalar register (one scalar operand per VALU instruction)
+    float c;
+    asm("v_mov_b32 %0, %1" : "=v"(c) : "s"(p.c_log2));
     const float lazy = kLazy / p.c_log2;
 
     for (int qt0 = 0; qt0 < nq; qt0 += QT) {
@@ -531,14 +548,14 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
         auto fold = [&](float x, bool mn) {
             float a, b;
             if constexpr (LPK == 8)
-                x = mn ? min2(x, ror8(x)) : x + ror8(x);
+                x = mn ? vmin(x, ror8(x)) : x + ror8(x);
             if constexpr (R <= 2) {
                 swap16(x, a, b);
-                x = mn ? min2(a, b) : a + b;
+                x = mn ? vmin(a, b) : a + b;
             }
             if constexpr (R == 1) {
                 swap32(x, a, b);
-                x = mn ? min2(a, b) : a + b;
+                x = mn ? vmin(a, b) : a + b;
             }
             return x;
         };
@@ -617,49 +634,43 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
         report(p.err, errbits);
 }
 
-// Query vectors per pass: 4, or 8 when a segment can have more than 4 (not
-// at D = 256, where 8 would not fit in registers).  Each query vector's
-// arithmetic is the same whatever the pass width.
+// One pass of 4 query vectors: this kernel serves the segments with at most
+// kMfmaMinQ (= 4) query vectors per kv head; the rest take rows_mfma_kernel.
+static_assert(kMfmaMinQ <= 4, "the decode kernel is launched for 4 query vectors a pass");
+
 template <int D, int KIND>
-hipError_t launch_qt(const RowsParams &p, int qt, dim3 grid, hipStream_t st)
+hipError_t launch_qt(const RowsParams &p, dim3 grid, hipStream_t st)
 {
-    if constexpr (D == 256) {
-        hipLaunchKernelGGL((rows_valu_kernel<D, KIND, 4>), grid, dim3(kThreads), 0, st, p);
-    } else {
-        if (qt <= 4)
-            hipLaunchKernelGGL((rows_valu_kernel<D, KIND, 4>), grid, dim3(kThreads), 0, st, p);
-        else
-            hipLaunchKernelGGL((rows_valu_kernel<D, KIND, 8>), grid, dim3(kThreads), 0, st, p);
-    }
+    hipLaunchKernelGGL((rows_valu_kernel<D, KIND, 4>), grid, dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_kind(const RowsParams &p, int kind, int qt, dim3 grid, hipStream_t st)
+hipError_t launch_kind(const RowsParams &p, int kind, dim3 grid, hipStream_t st)
 {
     switch (kind) {
     case TF_KV_CONTIG:
-        return launch_qt<D, TF_KV_CONTIG>(p, qt, grid, st);
+        return launch_qt<D, TF_KV_CONTIG>(p, grid, st);
     case TF_KV_PAGED:
-        return launch_qt<D, TF_KV_PAGED>(p, qt, grid, st);
+        return launch_qt<D, TF_KV_PAGED>(p, grid, st);
     default:
-        return launch_qt<D, TF_KV_RING>(p, qt, grid, st);
+        return launch_qt<D, TF_KV_RING>(p, grid, st);
     }
 }
 
 }  // namespace
 
 // Launch the VALU rows kernel; one block per (split, segment, kv head).
-hipError_t launch_rows_valu(const RowsParams &p, int head_dim, int kind, int qt, hipStream_t st)
+hipError_t launch_rows_valu(const RowsParams &p, int head_dim, int kind, hipStream_t st)
 {
     const dim3 grid((unsigned)(p.n_segments * p.n_split_max * p.hkv));
     switch (head_dim) {
     case 64:
-        return launch_kind<64>(p, kind, qt, grid, st);
+        return launch_kind<64>(p, kind, grid, st);
     case 128:
-        return launch_kind<128>(p, kind, qt, grid, st);
+        return launch_kind<128>(p, kind, grid, st);
     default:
-        return launch_kind<256>(p, kind, qt, grid, st);
+        return launch_kind<256>(p, kind, grid, st);
     }
 }
 
