@@ -86,6 +86,50 @@ def cpu_baseline(w, budget_s: float):
             "rows_per_s": round(nrows * reps / el, 2)}
 
 
+def bench_kv_put(args, w, dw, copies, stream) -> int:
+    """tf_kv_put of every segment's round rows (its last n_rows keys), timed
+    back to back; bytes = the rows' K and V read once and written once."""
+    import numpy as np
+    import torch
+    from stream_paged_attention_amd import binding
+    rng = np.random.Generator(np.random.PCG64(args.config + 100))
+    shape = (w.total_rows, w.n_kv_heads, w.head_dim)
+    k_new = torch.from_numpy(rng.integers(0, 1 << 16, size=shape, dtype=np.uint16).view(np.int16)).to(dw.device)
+    v_new = torch.from_numpy(rng.integers(0, 1 << 16, size=shape, dtype=np.uint16).view(np.int16)).to(dw.device)
+    st = stream.cuda_stream
+    argl = [dw.put_args(k_new, v_new, c) for c in range(copies)]
+    for i in range(args.warmup):
+        assert binding.tf_kv_put(argl[i % copies], st) == 0
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        binding.tf_kv_put(argl[i % copies], st)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    assert dw.error_word() == 0
+    nbytes = 2 * 2 * w.total_rows * w.n_kv_heads * w.head_dim * 2
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": f"KV-append GB/s, synthetic workload {args.config}", "value": round(gbps, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": synth_title(args.config) + " (round rows appended)", "rows": w.total_rows,
+                   "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "bytes_per_step": nbytes,
+                   "rows_per_s": round(w.total_rows / (ms * 1e-3), 1)},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 3), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "tf_kv_put (kv_put_kernel)"},
+    }), flush=True)
+    return 0
+
+
+def synth_title(n: int) -> str:
+    from stream_paged_attention_amd import synth
+    return synth.CONFIG_TITLES[n]
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +141,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kernel-only", action="store_true",
                     help="time only tf_attn_rows launches (for profiler runs)")
+    ap.add_argument("--op", choices=["attn", "kv_put"], default="attn",
+                    help="kv_put: time tf_kv_put of the workload's round rows instead")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run 20 plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -139,6 +185,8 @@ def main() -> int:
         wsb = binding.tf_argmax_workspace_bytes(nrows, vocab)
         ws = torch.empty(wsb // 8 + 1, dtype=torch.int64, device=dev)
     split = dw.split_keys > 0
+    if args.op == "kv_put":
+        return bench_kv_put(args, w, dw, copies, stream)
 
     def step(i):
         a = argl[i % copies]

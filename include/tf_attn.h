@@ -186,6 +186,45 @@ int tf_argmax(const void *logits, int32_t n_rows, int32_t vocab, int64_t row_str
               int32_t *ids, uint8_t *flags, void *workspace, size_t workspace_bytes,
               hipStream_t stream);
 
+/*
+ * KV append (TensorFold PR #1653, the kernel that puts a chunk's K/V rows
+ * into the core pool's pages; PR #1562, the drafter's ring rows written at
+ * the ring's head with the wrap).
+ *
+ * tf_kv_put writes every segment's new keys and values into its storage.
+ * The new keys of a segment are its last n_rows logical keys,
+ * [key_count - n_rows, key_count) -- the keys tf_attn_rows gives the
+ * segment's rows (each row sees itself) -- so a round is: update the table,
+ * tf_kv_put, tf_attn_rows.  Row r of the segment comes from packed row
+ * row_offset + r of k_new / v_new, bf16 [total_rows][n_kv_heads][head_dim]
+ * (laid out like q).  Logical key j goes to
+ *     PAGED:  page pages[j / page_size], offset j % page_size;
+ *     RING:   slot (first + j) mod capacity;
+ *     CONTIG: row j;
+ * in the segment's k / v storage (which must be writable; layout as in
+ * tf_kv_kind).  No other storage byte is written.  Segments must not
+ * write the same storage row.  Per-segment problems set TF_ERR_* bits in
+ * *err and skip that segment (BAD_ROWS, PAST_PAGES, BAD_RING) or that
+ * row (BAD_PAGE); nothing is written out of bounds.  Returns TF_OK,
+ * TF_E_INVALID or TF_E_UNSUPPORTED (nothing launched).
+ */
+typedef struct tf_put_args {
+    int32_t kind;             /* tf_kv_kind                                                  */
+    int32_t n_segments;       /* >= 0                                                        */
+    int32_t total_rows;       /* packed rows of k_new and v_new                              */
+    int32_t max_rows;         /* >= every segment's n_rows (grid sizing only)                */
+    int32_t n_kv_heads;       /* Hkv                                                         */
+    int32_t head_dim;         /* 64, 128 or 256                                              */
+    int32_t page_size;        /* PAGED: keys per page (power of two, 32..1024)               */
+    int32_t pool_pages;       /* PAGED: pages in the pool                                    */
+    const tf_segment *segs;   /* device: n_segments entries (partial_offset unused)          */
+    const void *k_new;        /* device bf16 [total_rows][n_kv_heads][head_dim]              */
+    const void *v_new;        /* device bf16, same layout                                    */
+    int32_t *err;             /* device int32 error word, or NULL                            */
+} tf_put_args;
+
+int tf_kv_put(const tf_put_args *a, hipStream_t stream);
+
 /* Workspace bytes tf_argmax needs for n_rows rows of vocab logits. */
 size_t tf_argmax_workspace_bytes(int32_t n_rows, int32_t vocab);
 

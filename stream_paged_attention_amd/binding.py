@@ -30,7 +30,7 @@ TF_ERR_BAD_RING = 8
 TF_ERR_PARTIALS = 16
 
 EXPORTS = ("tf_attn_rows", "tf_attn_merge", "tf_argmax", "tf_argmax_workspace_bytes",
-           "tf_plan_partials", "tf_check_segments", "tf_strerror")
+           "tf_kv_put", "tf_plan_partials", "tf_check_segments", "tf_strerror")
 
 
 class tf_segment(ctypes.Structure):
@@ -50,6 +50,15 @@ class tf_attn_args(ctypes.Structure):
                 ("split_keys", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("segs", ctypes.c_void_p), ("q", ctypes.c_void_p), ("out", ctypes.c_void_p),
                 ("partials", ctypes.c_void_p), ("partials_bytes", ctypes.c_size_t),
+                ("err", ctypes.c_void_p)]
+
+
+class tf_put_args(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("n_segments", ctypes.c_int32),
+                ("total_rows", ctypes.c_int32), ("max_rows", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("pool_pages", ctypes.c_int32),
+                ("segs", ctypes.c_void_p), ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
                 ("err", ctypes.c_void_p)]
 
 
@@ -76,6 +85,8 @@ def load(path: str = LIB_PATH):
     lib.tf_argmax.argtypes = [vp, i32, i32, ctypes.c_int64, vp, vp, vp, sz, vp]
     lib.tf_argmax_workspace_bytes.restype = sz
     lib.tf_argmax_workspace_bytes.argtypes = [i32, i32]
+    lib.tf_kv_put.restype = ctypes.c_int
+    lib.tf_kv_put.argtypes = [ctypes.POINTER(tf_put_args), vp]
     lib.tf_plan_partials.restype = ctypes.c_int
     lib.tf_plan_partials.argtypes = [ctypes.POINTER(tf_segment), i32, i32, i32, i32,
                                      ctypes.POINTER(sz)]
@@ -104,6 +115,10 @@ def tf_argmax(logits: int, n_rows: int, vocab: int, row_stride: int, ids: int, f
 
 def tf_argmax_workspace_bytes(n_rows: int, vocab: int, lib=None) -> int:
     return int((lib or load()).tf_argmax_workspace_bytes(n_rows, vocab))
+
+
+def tf_kv_put(args: tf_put_args, stream: int, lib=None) -> int:
+    return (lib or load()).tf_kv_put(ctypes.byref(args), ctypes.c_void_p(stream))
 
 
 def tf_plan_partials(segs, n_q_heads: int, head_dim: int, split_keys: int, lib=None):

@@ -192,6 +192,40 @@ class DeviceWorkload:
         torch.cuda.synchronize(self.device)
         return to_host_u16(out)
 
+    def put_args(self, k_new: torch.Tensor, v_new: torch.Tensor, copy: int = 0) -> binding.tf_put_args:
+        """tf_kv_put arguments writing packed new rows into this workload's storage."""
+        w = self.w
+        a = binding.tf_put_args()
+        a.kind = self.kind
+        a.n_segments = len(w.segments)
+        a.total_rows = w.total_rows
+        a.max_rows = w.max_rows
+        a.n_kv_heads = w.n_kv_heads
+        a.head_dim = w.head_dim
+        a.page_size = w.page_size if w.kind == "paged" else 0
+        a.pool_pages = w.pool_pages if w.kind == "paged" else 0
+        a.segs = self.tables[copy].data_ptr()
+        a.k_new = k_new.data_ptr()
+        a.v_new = v_new.data_ptr()
+        a.err = self.err.data_ptr()
+        return a
+
+    def kv_put(self, k_new: np.ndarray, v_new: np.ndarray, copy: int = 0) -> None:
+        """tf_kv_put of packed new rows [total_rows][Hkv][D] (bf16 bits) into copy `copy`."""
+        kn, vn = _dev(k_new, self.device), _dev(v_new, self.device)
+        st = torch.cuda.current_stream(self.device).cuda_stream
+        check(binding.tf_kv_put(self.put_args(kn, vn, copy), st), "tf_kv_put")
+        torch.cuda.synchronize(self.device)
+
+    def storage(self, copy: int = 0):
+        """Host copies of (K, V) storage: the pools, or lists of per-stream buffers."""
+        torch.cuda.synchronize(self.device)
+        k = [to_host_u16(x) for x in self.k_store[copy]]
+        v = [to_host_u16(x) for x in self.v_store[copy]]
+        if self.w.kind == "paged":
+            return k[0], v[0]
+        return k, v
+
     def partial_records(self) -> np.ndarray:
         """The partials workspace as [records][head_dim + 4] float32 (host copy)."""
         torch.cuda.synchronize(self.device)

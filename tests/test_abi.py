@@ -190,3 +190,17 @@ def test_argmax_refusals():
     assert binding.tf_argmax(0x100, 2, 10, 10, 0x200, 0x300, 0x400, 1, 0) == binding.TF_E_WORKSPACE
     assert binding.tf_argmax(0, 0, 10, 10, 0, 0, 0, 0, 0) == binding.TF_OK   # no rows: nothing to do
     assert binding.tf_argmax_workspace_bytes(32, 128000) == 32 * 16 * 12
+
+
+def test_put_refusals():
+    # refused before any launch: no GPU needed
+    a = binding.tf_put_args()
+    a.kind = binding.TF_KV_PAGED
+    a.n_segments, a.total_rows, a.max_rows, a.n_kv_heads, a.head_dim = 1, 1, 1, 2, 96
+    a.page_size, a.pool_pages = 32, 4
+    a.segs = a.k_new = a.v_new = 0x10000
+    assert binding.tf_kv_put(a, 0) == binding.TF_E_UNSUPPORTED
+    a.head_dim, a.page_size = 128, 48
+    assert binding.tf_kv_put(a, 0) == binding.TF_E_UNSUPPORTED
+    a.page_size, a.k_new = 32, 0x10008
+    assert binding.tf_kv_put(a, 0) == binding.TF_E_INVALID
