@@ -24,7 +24,11 @@
  *  - TensorFold PR #1562, "Qwen3.6 MTP drafter on CUDA: draft a shared
  *    round's streams together": the rows kernel that reads each row's ring,
  *    slots and segment from a table and must equal one launch per segment;
- *    ring slots folded in groups with the next group in flight.
+ *    ring slots folded in groups with the next group in flight; the tree
+ *    attention kernel beside it, whose trees equal their chains.
+ *  - TensorFold PR #1394, "lfm2: a cheaper DSpark hold": the drafter's block
+ *    attention, the target's kernels with a FULL flag under which every row
+ *    of a block sees the block's whole key range.
  *
  * Conventions
  *  - All tensors are bf16 (stored as 16-bit patterns), accumulation is fp32,
@@ -66,6 +70,15 @@ typedef enum tf_kv_kind {
                       /* slots; logical key j is in slot (first + j) mod capacity            */
 } tf_kv_kind;
 
+/* Which keys a row sees (one mask per launch).  Row r of an n-row segment: */
+typedef enum tf_mask {
+    TF_MASK_CAUSAL = 0, /* keys [0, key_count - n + r + 1): up to and including its own     */
+    TF_MASK_FULL = 1,   /* keys [0, key_count): a non-causal block (PR #1394, FULL flag)      */
+    TF_MASK_TREE = 2    /* keys [0, key_count - n), its own key key_count - n + r, and key
+                           key_count - n + j for every bit j set in tree[row_offset + r];
+                           needs n <= 64 (PR #1562, tree attention)                         */
+} tf_mask;
+
 /* Return codes. */
 enum {
     TF_OK = 0,
@@ -81,7 +94,8 @@ enum {
 enum {
     TF_ERR_PAST_PAGES = 1, /* key_count > capacity (x page_size for PAGED)                       */
     TF_ERR_BAD_PAGE = 2,   /* a page id outside [0, pool_pages)                                  */
-    TF_ERR_BAD_ROWS = 4,   /* n_rows < 1, n_rows > key_count, or rows outside [0, total_rows)    */
+    TF_ERR_BAD_ROWS = 4,   /* n_rows < 1, n_rows > key_count, rows outside [0, total_rows), or
+                              n_rows > 64 under TF_MASK_TREE                                   */
     TF_ERR_BAD_RING = 8,   /* ring first outside [0, capacity)                                   */
     TF_ERR_PARTIALS = 16   /* the segment's partial records fall outside the workspace           */
 };
@@ -90,9 +104,10 @@ enum {
  * One stream's span of a shared launch.  The table (an array of these)
  * lives in device memory.  48 bytes, 8-byte aligned.
  *
- * Row r (0-based) of an n-row segment is packed query row row_offset + r; it
- * sees logical keys [0, key_count - n_rows + r + 1): the segment's new rows
- * are its newest keys and each row sees itself (causal count).
+ * Row r (0-based) of an n-row segment is packed query row row_offset + r.
+ * The segment's new rows are its newest keys: row r's own key is logical key
+ * key_count - n_rows + r.  Which keys it sees is the launch's tf_mask
+ * (causal count: [0, key_count - n_rows + r + 1)).
  */
 typedef struct tf_segment {
     const void *k;          /* bf16 K storage (see tf_kv_kind)                                 */
@@ -102,7 +117,7 @@ typedef struct tf_segment {
     int32_t first;          /* RING: slot that holds logical key 0; 0 otherwise                */
     int32_t row_offset;     /* first packed query row of this segment                          */
     int32_t n_rows;         /* 1 <= n_rows <= key_count                                        */
-    int32_t key_count;      /* keys visible to the segment's last row                          */
+    int32_t key_count;      /* keys of the stream, the segment's new rows included             */
     int32_t partial_offset; /* first partial record of this segment (see tf_plan_partials)     */
 } tf_segment;
 
@@ -113,8 +128,8 @@ typedef struct tf_segment {
  * Partial records: record index
  *     partial_offset + (r * n_q_heads + h) * n_splits + t,
  * with n_splits = ceil(key_count / split_keys) of the record's segment,
- * holds split t (keys [t * split_keys, (t + 1) * split_keys) of row r's
- * visible keys) of row r, query head h.  A record is head_dim + 4 floats:
+ * holds split t (the keys in [t * split_keys, (t + 1) * split_keys) that
+ * row r sees) of row r, query head h.  A record is head_dim + 4 floats:
  *     [0] m  : reference for the split's scaled scores (natural-log units):
  *              one of them, at most 8 ln 2 below their max (so no weight
  *              exceeds 2^8); -inf if the split is empty, NaN if it saw a
@@ -142,7 +157,11 @@ typedef struct tf_attn_args {
     int32_t split_keys;       /* keys per partial (multiple of 32), or 0 = one split: then
                                  tf_attn_rows writes out directly and needs no partials      */
     float scale;              /* score = scale * (q . k), finite and > 0, normally 1/sqrt(D) */
+    int32_t mask;             /* tf_mask                                                     */
     const tf_segment *segs;   /* device: n_segments entries                                  */
+    const uint64_t *tree;     /* TF_MASK_TREE: device, one ancestor mask per packed row (bit j
+                                 = the segment's row j is on the row's path to its root);
+                                 ignored otherwise                                           */
     const void *q;            /* device bf16 [total_rows][n_q_heads][head_dim]               */
     void *out;                /* device bf16 [total_rows][n_q_heads][head_dim]               */
     float *partials;          /* device fp32 records (split_keys > 0)                        */

@@ -15,10 +15,16 @@
  *    a float64 attention; TensorFold PR #1562 ("Qwen3.6 MTP drafter on CUDA:
  *    draft a shared round's streams together"), its Gate section (FP64 check
  *    at the served shapes).
- *  - Causal count: a row sees the keys up to and including its own position
- *    (TensorFold PR #1394, "lfm2: a cheaper DSpark hold", the DSpark drafter
- *    commit contrasting the FULL block flag with the target's causal count).
- *    Row r of an n-row segment with key_count kc sees keys [0, kc - n + r + 1).
+ *  - Which keys a row sees (TensorFold PR #1394, "lfm2: a cheaper DSpark
+ *    hold", the DSpark drafter commit contrasting the FULL block flag with
+ *    the target's causal count; PR #1562, the Qwen3.6 MTP drafter's tree
+ *    attention beside its chains).  Row r of an n-row segment with
+ *    key_count kc sees, by the launch's mask:
+ *      causal: keys [0, kc - n + r + 1) (up to and including its own key);
+ *      full:   keys [0, kc) (every row of the block sees the whole range);
+ *      tree:   the context keys [0, kc - n), its own key kc - n + r, and the
+ *              key kc - n + j of every row j whose bit is set in the row's
+ *              64-bit ancestor mask (n <= 64).
  *  - Split-K partials and their merge (PR #1503, the shared-window chunk and
  *    merge bodies; PR #1653, "spark25 CUDA: the full layers' caches in pages
  *    of the core pool", the paged decode part/merge kernels).
@@ -33,7 +39,7 @@
  *    of that (row, head)'s outputs are NaN; otherwise an output element whose
  *    value is not finite is reported as NaN.  Keys outside the visible range
  *    are never read.
- *  - Empty split (its first key is past the row's causal limit): m = -inf,
+ *  - Empty split (the row sees none of the keys it covers): m = -inf,
  *    l = 0, o = 0, and the merge skips it.
  *
  * Inputs are bf16 bit patterns (uint16).  K and V are each stream's logical
@@ -61,16 +67,41 @@ static double bf16_value(uint16_t bits)
     return (double)f;
 }
 
+enum { MASK_CAUSAL = 0, MASK_FULL = 1, MASK_TREE = 2 };
+
 /* One (row, head) task: where its query is and which keys it may see. */
 typedef struct {
     int64_t qrow;      /* packed row index */
     int head;          /* query head */
     int seg;           /* segment */
-    int visible;       /* number of visible keys (causal limit) */
+    int row;           /* row within its segment */
+    int n_rows;        /* rows of its segment */
+    int key_count;     /* keys of its stream */
+    int mask;          /* MASK_* */
+    uint64_t anc;      /* tree: bit j = the segment's row j is an ancestor */
 } task_t;
 
+/* Whether the task's row sees key j of its stream (the masks above). */
+static int sees(const task_t *t, int j)
+{
+    const int first_new = t->key_count - t->n_rows;   /* key of the segment's row 0 */
+    if (j < 0 || j >= t->key_count)
+        return 0;
+    switch (t->mask) {
+    case MASK_FULL:
+        return 1;
+    case MASK_TREE:
+        if (j < first_new || j == first_new + t->row)
+            return 1;
+        return (int)((t->anc >> (j - first_new)) & 1u);
+    default:
+        return j <= first_new + t->row;
+    }
+}
+
 static task_t *make_tasks(int n_seg, const int32_t *n_rows, const int32_t *key_count,
-                          const int32_t *row_offset, int hq, int64_t *n_tasks)
+                          const int32_t *row_offset, int hq, int mask, const uint64_t *tree,
+                          int64_t *n_tasks)
 {
     int64_t total = 0;
     for (int s = 0; s < n_seg; ++s)
@@ -83,7 +114,11 @@ static task_t *make_tasks(int n_seg, const int32_t *n_rows, const int32_t *key_c
                 t[at].qrow = (int64_t)row_offset[s] + r;
                 t[at].head = h;
                 t[at].seg = s;
-                t[at].visible = key_count[s] - n_rows[s] + r + 1;
+                t[at].row = r;
+                t[at].n_rows = n_rows[s];
+                t[at].key_count = key_count[s];
+                t[at].mask = mask;
+                t[at].anc = mask == MASK_TREE ? tree[row_offset[s] + r] : 0;
                 ++at;
             }
     *n_tasks = total;
@@ -100,20 +135,26 @@ static int threads_used(int n_threads)
 #endif
 }
 
-/* Scores of one query against keys [j0, j1) of its stream, in double. */
-static int scores_into(const uint16_t *q, const uint16_t *k, int hkv, int d, int g,
-                       int j0, int j1, double scale, double *qd, double *s)
+/* Scores of one query against the keys j in [j0, j1) its task sees, in
+ * double (s[j - j0]; entries of unseen keys are left alone).  Returns 1 if
+ * a seen score is not finite; *n_seen counts the seen keys. */
+static int scores_into(const task_t *t, const uint16_t *q, const uint16_t *k, int hkv, int d,
+                       int g, int j0, int j1, double scale, double *qd, double *s, int *n_seen)
 {
     int nonfinite = 0;
+    *n_seen = 0;
     for (int x = 0; x < d; ++x)
         qd[x] = bf16_value(q[x]);
     for (int j = j0; j < j1; ++j) {
+        if (!sees(t, j))
+            continue;
         const uint16_t *kr = k + ((int64_t)j * hkv + g) * d;
         double acc = 0.0;
         for (int x = 0; x < d; ++x)
             acc += qd[x] * bf16_value(kr[x]);
         acc *= scale;
         s[j - j0] = acc;
+        ++*n_seen;
         if (!isfinite(acc))
             nonfinite = 1;
     }
@@ -129,10 +170,10 @@ int oracle_attn(int n_seg, const int32_t *n_rows, const int32_t *key_count,
                 const int32_t *row_offset, const int64_t *key_base,
                 int hq, int hkv, int d, double scale,
                 const uint16_t *q, const uint16_t *k_all, const uint16_t *v_all,
-                double *out, int n_threads)
+                int mask, const uint64_t *tree, double *out, int n_threads)
 {
     int64_t nt = 0;
-    task_t *tasks = make_tasks(n_seg, n_rows, key_count, row_offset, hq, &nt);
+    task_t *tasks = make_tasks(n_seg, n_rows, key_count, row_offset, hq, mask, tree, &nt);
     int maxkc = 1;
     for (int s = 0; s < n_seg; ++s)
         if (key_count[s] > maxkc)
@@ -153,19 +194,23 @@ int oracle_attn(int n_seg, const int32_t *n_rows, const int32_t *key_count,
             const uint16_t *ks = k_all + key_base[t->seg] * hkv * d;
             const uint16_t *vs = v_all + key_base[t->seg] * hkv * d;
             double *o = out + (t->qrow * hq + t->head) * d;
-            if (scores_into(qv, ks, hkv, d, g, 0, t->visible, scale, qd, s)) {
+            int n_seen = 0;
+            if (scores_into(t, qv, ks, hkv, d, g, 0, t->key_count, scale, qd, s, &n_seen) ||
+                n_seen == 0) {
                 for (int x = 0; x < d; ++x)
                     o[x] = NAN;
                 continue;
             }
             double m = -INFINITY;
-            for (int j = 0; j < t->visible; ++j)
-                if (s[j] > m)
+            for (int j = 0; j < t->key_count; ++j)
+                if (sees(t, j) && s[j] > m)
                     m = s[j];
             double l = 0.0;
             for (int x = 0; x < d; ++x)
                 acc[x] = 0.0;
-            for (int j = 0; j < t->visible; ++j) {
+            for (int j = 0; j < t->key_count; ++j) {
+                if (!sees(t, j))
+                    continue;
                 const double p = exp(s[j] - m);
                 const uint16_t *vr = vs + ((int64_t)j * hkv + g) * d;
                 l += p;
@@ -186,8 +231,8 @@ int oracle_attn(int n_seg, const int32_t *n_rows, const int32_t *key_count,
 }
 
 /*
- * oracle_attn_partials: split-K pieces.  Split t of a row covers keys
- * [t*split, min((t+1)*split, visible)).  For each (row, head, split):
+ * oracle_attn_partials: split-K pieces.  Split t of a row covers the keys
+ * it sees in [t*split, (t+1)*split).  For each (row, head, split):
  *   m = max score, l = sum exp(score - m), o = sum exp(score - m) v.
  * Layout: m, l [total_rows][hq][n_split]; o [total_rows][hq][n_split][d].
  * A split holding a nonfinite visible score is all NaN; an empty split is
@@ -197,11 +242,11 @@ int oracle_attn_partials(int n_seg, const int32_t *n_rows, const int32_t *key_co
                          const int32_t *row_offset, const int64_t *key_base,
                          int hq, int hkv, int d, double scale,
                          const uint16_t *q, const uint16_t *k_all, const uint16_t *v_all,
-                         int split, int n_split,
+                         int mask, const uint64_t *tree, int split, int n_split,
                          double *pm, double *pl, double *po, int n_threads)
 {
     int64_t nt = 0;
-    task_t *tasks = make_tasks(n_seg, n_rows, key_count, row_offset, hq, &nt);
+    task_t *tasks = make_tasks(n_seg, n_rows, key_count, row_offset, hq, mask, tree, &nt);
     const int group = hq / hkv;
     const int used = threads_used(n_threads);
 
@@ -220,17 +265,17 @@ int oracle_attn_partials(int n_seg, const int32_t *n_rows, const int32_t *key_co
                 const int64_t rec = (t->qrow * hq + t->head) * n_split + sp;
                 double *o = po + rec * d;
                 const int j0 = sp * split;
-                int j1 = j0 + split;
-                if (j1 > t->visible)
-                    j1 = t->visible;
-                if (j0 >= j1) {
+                const int j1 = j0 + split;
+                int n_seen = 0;
+                const int bad = scores_into(t, qv, ks, hkv, d, g, j0, j1, scale, qd, s, &n_seen);
+                if (n_seen == 0) {
                     pm[rec] = -INFINITY;
                     pl[rec] = 0.0;
                     for (int x = 0; x < d; ++x)
                         o[x] = 0.0;
                     continue;
                 }
-                if (scores_into(qv, ks, hkv, d, g, j0, j1, scale, qd, s)) {
+                if (bad) {
                     pm[rec] = NAN;
                     pl[rec] = NAN;
                     for (int x = 0; x < d; ++x)
@@ -239,12 +284,14 @@ int oracle_attn_partials(int n_seg, const int32_t *n_rows, const int32_t *key_co
                 }
                 double m = -INFINITY;
                 for (int j = j0; j < j1; ++j)
-                    if (s[j - j0] > m)
+                    if (sees(t, j) && s[j - j0] > m)
                         m = s[j - j0];
                 double l = 0.0;
                 for (int x = 0; x < d; ++x)
                     o[x] = 0.0;
                 for (int j = j0; j < j1; ++j) {
+                    if (!sees(t, j))
+                        continue;
                     const double p = exp(s[j - j0] - m);
                     const uint16_t *vr = vs + ((int64_t)j * hkv + g) * d;
                     l += p;

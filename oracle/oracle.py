@@ -54,14 +54,16 @@ def _declare(lib) -> None:
     u16p = ctypes.POINTER(ctypes.c_uint16)
     f64p = ctypes.POINTER(ctypes.c_double)
     lib.oracle_attn.restype = ctypes.c_int
+    u64p = ctypes.POINTER(ctypes.c_uint64)
     lib.oracle_attn.argtypes = [ctypes.c_int, i32p, i32p, i32p, i64p, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_int, ctypes.c_double, u16p, u16p,
-                                u16p, f64p, ctypes.c_int]
+                                u16p, ctypes.c_int, u64p, f64p, ctypes.c_int]
     lib.oracle_attn_partials.restype = ctypes.c_int
     lib.oracle_attn_partials.argtypes = [ctypes.c_int, i32p, i32p, i32p, i64p,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_double, u16p, u16p, u16p, ctypes.c_int,
-                                         ctypes.c_int, f64p, f64p, f64p, ctypes.c_int]
+                                         u64p, ctypes.c_int, ctypes.c_int, f64p, f64p, f64p,
+                                         ctypes.c_int]
     lib.oracle_merge.restype = None
     lib.oracle_merge.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, f64p, f64p,
                                  f64p, f64p]
@@ -72,6 +74,20 @@ def _declare(lib) -> None:
 
 def _p(a: np.ndarray, ct):
     return a.ctypes.data_as(ctypes.POINTER(ct))
+
+
+MASKS = {"causal": 0, "full": 1, "tree": 2}
+
+
+def _mask_args(mask: str, tree, n_total_rows: int):
+    """(mask code, uint64 ancestor masks per packed row, kept alive by the caller)."""
+    code = MASKS[mask]
+    if code == MASKS["tree"]:
+        t = np.ascontiguousarray(tree, dtype=np.uint64)
+        assert t.shape == (n_total_rows,)
+    else:
+        t = np.zeros(1, dtype=np.uint64)
+    return code, t
 
 
 def _concat(arrs):
@@ -93,12 +109,14 @@ def _layout(n_rows: Sequence[int], key_counts: Sequence[int], k_logical, v_logic
 
 
 def attn_raw(n_rows, key_counts, row_offsets, key_base, q, k_all, v_all, *, n_q_heads,
-             n_kv_heads, head_dim, scale, threads: int = 0, lib=None):
+             n_kv_heads, head_dim, scale, mask: str = "causal", tree=None, threads: int = 0,
+             lib=None):
     """Unsplit attention over explicit per-segment offsets.
 
     Segment s reads query rows ``row_offsets[s] ..`` of ``q`` and keys
     ``key_base[s] ..`` of the concatenated logical ``k_all``/``v_all``.
-    Returns ``(out, threads_used)``.
+    ``mask`` is "causal", "full" or "tree" (then ``tree`` holds one uint64
+    ancestor mask per row of ``q``).  Returns ``(out, threads_used)``.
     """
     lib = lib or _load()
     assert n_q_heads % n_kv_heads == 0
@@ -114,29 +132,34 @@ def attn_raw(n_rows, key_counts, row_offsets, key_base, q, k_all, v_all, *, n_q_
     assert int((offs + nr).max()) <= q.shape[0]
     assert int((base + kcs).max()) <= k_all.shape[0] and k_all.shape == v_all.shape
     assert k_all.shape[1:] == (n_kv_heads, head_dim)
+    if mask == "tree":
+        assert int(nr.max()) <= 64
+    code, tr = _mask_args(mask, tree, q.shape[0])
     out = np.full((q.shape[0], n_q_heads, head_dim), np.nan, dtype=np.float64)
     used = lib.oracle_attn(len(nr), _p(nr, ctypes.c_int32), _p(kcs, ctypes.c_int32),
                            _p(offs, ctypes.c_int32), _p(base, ctypes.c_int64), n_q_heads,
                            n_kv_heads, head_dim, float(scale), _p(q, ctypes.c_uint16),
-                           _p(k_all, ctypes.c_uint16), _p(v_all, ctypes.c_uint16),
-                           _p(out, ctypes.c_double), int(threads))
+                           _p(k_all, ctypes.c_uint16), _p(v_all, ctypes.c_uint16), code,
+                           _p(tr, ctypes.c_uint64), _p(out, ctypes.c_double), int(threads))
     return out, used
 
 
 def attn(n_rows, key_counts, q, k_logical, v_logical, *, n_q_heads, n_kv_heads, head_dim,
-         scale, threads: int = 0, return_threads: bool = False, lib=None):
+         scale, mask: str = "causal", tree=None, threads: int = 0,
+         return_threads: bool = False, lib=None):
     """Unsplit softmax attention in float64 -> ``[total_rows][Hq][D]``."""
     nr, kcs, offs, base, k_all, v_all = _layout(n_rows, key_counts, k_logical, v_logical)
     q = np.ascontiguousarray(q, dtype=np.uint16)
     assert q.shape[0] == int(nr.sum())
     out, used = attn_raw(nr, kcs, offs, base, q, k_all, v_all, n_q_heads=n_q_heads,
-                         n_kv_heads=n_kv_heads, head_dim=head_dim, scale=scale,
-                         threads=threads, lib=lib)
+                         n_kv_heads=n_kv_heads, head_dim=head_dim, scale=scale, mask=mask,
+                         tree=tree, threads=threads, lib=lib)
     return (out, used) if return_threads else out
 
 
 def attn_partials(n_rows, key_counts, q, k_logical, v_logical, *, n_q_heads, n_kv_heads,
-                  head_dim, scale, split, threads: int = 0, lib=None):
+                  head_dim, scale, split, mask: str = "causal", tree=None, threads: int = 0,
+                  lib=None):
     """Split-K partials in float64.
 
     Returns ``(m, l, o)`` with shapes ``[rows][Hq][n_split]`` and
@@ -150,11 +173,12 @@ def attn_partials(n_rows, key_counts, q, k_logical, v_logical, *, n_q_heads, n_k
     m = np.empty((total, n_q_heads, n_split), dtype=np.float64)
     l = np.empty_like(m)
     o = np.empty((total, n_q_heads, n_split, head_dim), dtype=np.float64)
+    code, tr = _mask_args(mask, tree, total)
     lib.oracle_attn_partials(len(nr), _p(nr, ctypes.c_int32), _p(kcs, ctypes.c_int32),
                              _p(offs, ctypes.c_int32), _p(base, ctypes.c_int64), n_q_heads,
                              n_kv_heads, head_dim, float(scale), _p(q, ctypes.c_uint16),
-                             _p(k_all, ctypes.c_uint16), _p(v_all, ctypes.c_uint16),
-                             int(split), n_split, _p(m, ctypes.c_double),
+                             _p(k_all, ctypes.c_uint16), _p(v_all, ctypes.c_uint16), code,
+                             _p(tr, ctypes.c_uint64), int(split), n_split, _p(m, ctypes.c_double),
                              _p(l, ctypes.c_double), _p(o, ctypes.c_double), int(threads))
     return m, l, o
 
@@ -190,10 +214,14 @@ def argmax(logits: np.ndarray, vocab: int | None = None, lib=None):
 def attn_workload(w, rows=None, threads: int = 0, return_threads: bool = False):
     """Oracle output for a synthetic workload (all rows, or a sample of packed rows).
 
-    A sampled row r of an n-row segment is evaluated as a one-row segment over
-    the first ``kc - n + r + 1`` logical keys of its stream: the same visible
-    set.  With ``rows`` given, the result has one entry per sampled row.
+    The workload's ``mask`` ("causal", "full" or "tree", with ``tree`` the
+    ancestor masks) picks the keys each row sees.  A sampled row r of an
+    n-row segment is evaluated as a one-row segment over the keys it sees when
+    those are a prefix of its stream: the first ``kc - n + r + 1`` (causal) or
+    all ``kc`` (full).  Under a tree mask the sampled rows' whole segments are
+    evaluated.  With ``rows`` given, the result has one entry per sampled row.
     """
+    mask = getattr(w, "mask", "causal")
     kw = dict(n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
               scale=w.scale, threads=threads)
     kcs_all = [s.key_count for s in w.segments]
@@ -202,10 +230,12 @@ def attn_workload(w, rows=None, threads: int = 0, return_threads: bool = False):
         base_all[1:] = np.cumsum(np.asarray(kcs_all, dtype=np.int64))[:-1]
     k_all = _concat(w.k_logical)
     v_all = _concat(w.v_logical)
-    if rows is None:
+    if rows is None or mask == "tree":
         out, used = attn_raw([s.n_rows for s in w.segments], kcs_all,
                              [s.row_offset for s in w.segments], base_all, w.q, k_all, v_all,
-                             **kw)
+                             mask=mask, tree=getattr(w, "tree", None), **kw)
+        if rows is not None:
+            out = out[[int(r) for r in rows]]
         return (out, used) if return_threads else out
     seg_of = []
     for si, s in enumerate(w.segments):
@@ -216,7 +246,7 @@ def attn_workload(w, rows=None, threads: int = 0, return_threads: bool = False):
         si, r = seg_of[row]
         s = w.segments[si]
         n_rows.append(1)
-        kcs.append(s.key_count - s.n_rows + r + 1)
+        kcs.append(s.key_count if mask == "full" else s.key_count - s.n_rows + r + 1)
         offs.append(i)
         base.append(base_all[si])
     out, used = attn_raw(n_rows, kcs, offs, base, w.q[rows], k_all, v_all, **kw)

@@ -16,6 +16,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtfattn.s
 TF_KV_CONTIG, TF_KV_PAGED, TF_KV_RING = 0, 1, 2
 KIND_CODE = {"contig": TF_KV_CONTIG, "paged": TF_KV_PAGED, "ring": TF_KV_RING}
 
+TF_MASK_CAUSAL, TF_MASK_FULL, TF_MASK_TREE = 0, 1, 2
+MASK_CODE = {"causal": TF_MASK_CAUSAL, "full": TF_MASK_FULL, "tree": TF_MASK_TREE}
+
 TF_OK = 0
 TF_E_INVALID = -1
 TF_E_UNSUPPORTED = -2
@@ -48,7 +51,9 @@ class tf_attn_args(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("pool_pages", ctypes.c_int32),
                 ("split_keys", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("segs", ctypes.c_void_p), ("q", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("mask", ctypes.c_int32),
+                ("segs", ctypes.c_void_p), ("tree", ctypes.c_void_p),
+                ("q", ctypes.c_void_p), ("out", ctypes.c_void_p),
                 ("partials", ctypes.c_void_p), ("partials_bytes", ctypes.c_size_t),
                 ("err", ctypes.c_void_p)]
 

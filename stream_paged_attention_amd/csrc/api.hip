@@ -55,6 +55,8 @@ int check_args(const tf_attn_args *a, bool need_partials)
         return TF_E_UNSUPPORTED;
     if (!(a->scale > 0.0f && a->scale < 3.0e38f))   // also refuses NaN and +inf
         return TF_E_INVALID;
+    if (a->mask != TF_MASK_CAUSAL && a->mask != TF_MASK_FULL && a->mask != TF_MASK_TREE)
+        return TF_E_INVALID;
     if (a->n_segments == 0)
         return TF_OK;
     if (a->max_rows < 1 || a->max_keys < a->max_rows)
@@ -62,6 +64,9 @@ int check_args(const tf_attn_args *a, bool need_partials)
     if (a->segs == nullptr || a->q == nullptr || a->out == nullptr)
         return TF_E_INVALID;
     if (!aligned16(a->q) || !aligned16(a->out))
+        return TF_E_INVALID;
+    if (a->mask == TF_MASK_TREE &&
+        (a->tree == nullptr || (reinterpret_cast<uintptr_t>(a->tree) & 7u) != 0 || a->max_rows > 64))
         return TF_E_INVALID;
     const int64_t splits = n_splits_of(a->max_keys, a->split_keys);
     if ((int64_t)a->n_segments * splits > 0x7FFFFFFF || (int64_t)a->n_segments * a->max_rows > 0x7FFFFFFF)
@@ -100,6 +105,8 @@ tfa::RowsParams make_params(const tf_attn_args *a)
     p.n_split_max = n_splits_of(a->max_keys, a->split_keys);
     p.c_log2 = (float)((double)a->scale * 1.4426950408889634073599);
     p.mfma_min_q = tfa::kMfmaMinQ;
+    p.mask = a->mask;
+    p.tree = a->mask == TF_MASK_TREE ? a->tree : nullptr;
     return p;
 }
 

@@ -35,7 +35,51 @@ struct RowsParams {
     float c_log2;          // scale * log2(e): scores are kept in base-2 units
     int mfma_min_q;        // segments with more query vectors per kv head than this
                            // (n_rows * group) take the matrix-core kernel
+    int mask;              // tf_mask
+    const uint64_t *tree;  // TF_MASK_TREE: ancestor mask per packed row
 };
+
+// Which keys row r of an n-row segment over kc keys sees (tf_mask), as
+// a limit and a tree test: key j counts when row_sees<MASK>(j, ...).
+// lim is one past the row's last seen key, cut at the split end k_end.
+// The mask is a template argument (one kernel instance each).  Under
+// TF_MASK_TREE tb = kc - n is the
+// first new key and anc holds the row's ancestors and itself; otherwise tb
+// is INT32_MAX and every key below lim counts.  Every key below
+// min(lim, tb) counts (unmasked tiles).
+struct RowVis {
+    int lim;
+    int tb;
+    uint64_t anc;
+};
+
+template <int MASK>
+__device__ __forceinline__ RowVis row_vis(const RowsParams &p, int kc, int n, int r, int row_offset,
+                                          int k_end)
+{
+    RowVis v;
+    v.tb = INT32_MAX;
+    v.anc = 0;
+    if constexpr (MASK == TF_MASK_TREE) {
+        v.tb = kc - n;
+        v.anc = p.tree[row_offset + r] | (1ull << r);
+        v.lim = min(v.tb + (64 - __clzll((long long)v.anc)), k_end);
+    } else if constexpr (MASK == TF_MASK_FULL) {
+        v.lim = k_end;
+    } else {
+        v.lim = min(kc - n + r + 1, k_end);
+    }
+    return v;
+}
+
+template <int MASK>
+__device__ __forceinline__ bool row_sees(int key, int lim, int tb, uint64_t anc)
+{
+    if constexpr (MASK == TF_MASK_TREE)
+        return key < lim && (key < tb || ((anc >> ((key - tb) & 63)) & 1ull) != 0);
+    else
+        return key < lim;
+}
 
 // Query vectors per kv head above which a segment is served by the MFMA
 // kernel (prompt chunks, long verify rounds); at or below, by the VALU kernel.

@@ -26,7 +26,8 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(RowsParams p, int ma
     const int n_rows = sd.n_rows, kc = sd.key_count, row_offset = sd.row_offset;
     if (r >= n_rows)
         return;
-    if (n_rows < 1 || n_rows > kc || row_offset < 0 || (int64_t)row_offset + n_rows > p.total_rows)
+    if (n_rows < 1 || n_rows > kc || row_offset < 0 || (int64_t)row_offset + n_rows > p.total_rows ||
+        (p.mask == TF_MASK_TREE && n_rows > 64))
         return;   // reported by tf_attn_rows; no row can be addressed safely
     const int n_splits = (kc + p.split_keys - 1) / p.split_keys;
     const int64_t first = (int64_t)sd.partial_offset + ((int64_t)r * p.hq + h) * n_splits;

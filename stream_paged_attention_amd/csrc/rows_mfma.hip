@@ -27,8 +27,8 @@
 // reading one unit column hit distinct banks.  NBUF tile buffers: NBUF - 1
 // tiles in flight while one is multiplied, one barrier per tile.
 //
-// Masking (causal rows, split end, keys past the count) happens on the
-// scores.  A masked key's value must add exactly nothing, but 0 * NaN = NaN
+// Masking (causal rows, a tree's block, split end, keys past the count)
+// happens on the scores.  A masked key's value must add exactly nothing, but 0 * NaN = NaN
 // on the matrix core: in tiles that mask anything, nonfinite value elements
 // are replaced by 0 before the product, and an indicator product records
 // which (dimension, query vector) outputs saw a nonfinite value among their
@@ -136,7 +136,7 @@ __device__ __forceinline__ void wait_tiles(int newer)
     }
 }
 
-template <int D, int KIND>
+template <int D, int KIND, int MASK>
 __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams p)
 {
     using G = MGeo<D>;
@@ -173,7 +173,8 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
     if (nq <= p.mfma_min_q)
         return;
     const bool rows_ok = n_rows >= 1 && n_rows <= kc && row_offset >= 0 &&
-                         (int64_t)row_offset + n_rows <= p.total_rows;
+                         (int64_t)row_offset + n_rows <= p.total_rows &&
+                         (MASK != TF_MASK_TREE || n_rows <= 64);
     if (!rows_ok) {
         if (threadIdx.x == 0 && g == 0 && t == 0 && qt == 0)
             report(p.err, TF_ERR_BAD_ROWS);
@@ -211,6 +212,8 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
     // ---- this lane's query vectors (one per 16-vector block) and limits
     const int qv0 = qt * QB + wave * (16 * NQB);
     int lim[NQB];
+    uint64_t anc[NQB];
+    int tb = INT32_MAX;   // the segment's first new key under a tree mask
     bool qvalid[NQB];
     int lim_min = INT32_MAX, lim_max = k0;
 #pragma unroll
@@ -218,13 +221,16 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
         const int qv = qv0 + b * 16 + lc;
         qvalid[b] = qv < nq;
         const int r = qv / group;
-        lim[b] = qvalid[b] ? min(kc - n_rows + r + 1, k_end) : 0;
+        const RowVis rv = row_vis<MASK>(p, kc, n_rows, qvalid[b] ? r : 0, row_offset, k_end);
+        lim[b] = qvalid[b] ? rv.lim : 0;
+        anc[b] = rv.anc;
+        tb = rv.tb;
     }
     // wave-wide visible range: tiles below lim_min are unmasked for every
     // query vector of the wave, tiles at or past lim_max are invisible
 #pragma unroll
     for (int b = 0; b < NQB; ++b) {
-        int lo_b = qvalid[b] ? lim[b] : INT32_MAX;
+        int lo_b = qvalid[b] ? min(lim[b], tb) : INT32_MAX;
         int hi_b = qvalid[b] ? lim[b] : k0;
         // reduce over the 64 lanes (the 4 lane groups hold the same values)
 #pragma unroll
@@ -417,7 +423,7 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
                     float x = s[b][kb][e];
                     if (!full) {
                         const int key = kt + kb * 16 + lg * 4 + e;
-                        const bool vis = key < lim[b];
+                        const bool vis = row_sees<MASK>(key, lim[b], tb, anc[b]);
                         lo[b] = min2(lo[b], vis ? x : INFINITY);
                         x = vis ? x : -INFINITY;
                         s[b][kb][e] = x;
@@ -517,7 +523,9 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
 #pragma unroll
                         for (int w = 0; w < 4; ++w) {
                             const int ka = kt + (w >> 1) * 16 + lg * 4 + (w & 1) * 2;
-                            visf[w] = (ka < lim[b] ? 0x3F80u : 0u) | (ka + 1 < lim[b] ? 0x3F800000u : 0u);
+                            const bool v0 = row_sees<MASK>(ka, lim[b], tb, anc[b]);
+                            const bool v1 = row_sees<MASK>(ka + 1, lim[b], tb, anc[b]);
+                            visf[w] = (v0 ? 0x3F80u : 0u) | (v1 ? 0x3F800000u : 0u);
                         }
                         const f32x4_t cnt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             as_bf16x8(ind), as_bf16x8(visf), f32x4_t{0, 0, 0, 0}, 0, 0, 0);
@@ -613,22 +621,33 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
         report(p.err, errbits);
 }
 
-template <int D>
-hipError_t launch_kind_m(const RowsParams &p, int kind, int n_qt, hipStream_t st)
+template <int D, int MASK>
+void launch_kind_m(const RowsParams &p, int kind, int n_qt, hipStream_t st)
 {
     const dim3 grid((unsigned)(n_qt * p.n_split_max * p.n_segments * p.hkv));
     const dim3 block(64 * MGeo<D>::NW);
     switch (kind) {
     case TF_KV_CONTIG:
-        hipLaunchKernelGGL((rows_mfma_kernel<D, TF_KV_CONTIG>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((rows_mfma_kernel<D, TF_KV_CONTIG, MASK>), grid, block, 0, st, p);
         break;
     case TF_KV_PAGED:
-        hipLaunchKernelGGL((rows_mfma_kernel<D, TF_KV_PAGED>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((rows_mfma_kernel<D, TF_KV_PAGED, MASK>), grid, block, 0, st, p);
         break;
     default:
-        hipLaunchKernelGGL((rows_mfma_kernel<D, TF_KV_RING>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((rows_mfma_kernel<D, TF_KV_RING, MASK>), grid, block, 0, st, p);
         break;
     }
+}
+
+template <int D>
+hipError_t launch_mask_m(const RowsParams &p, int kind, int n_qt, hipStream_t st)
+{
+    if (p.mask == TF_MASK_TREE)
+        launch_kind_m<D, TF_MASK_TREE>(p, kind, n_qt, st);
+    else if (p.mask == TF_MASK_FULL)
+        launch_kind_m<D, TF_MASK_FULL>(p, kind, n_qt, st);
+    else
+        launch_kind_m<D, TF_MASK_CAUSAL>(p, kind, n_qt, st);
     return hipGetLastError();
 }
 
@@ -649,11 +668,11 @@ hipError_t launch_rows_mfma(const RowsParams &p, int head_dim, int kind, int max
     const int n_qt = (max_q + qb - 1) / qb;
     switch (head_dim) {
     case 64:
-        return launch_kind_m<64>(p, kind, n_qt, st);
+        return launch_mask_m<64>(p, kind, n_qt, st);
     case 128:
-        return launch_kind_m<128>(p, kind, n_qt, st);
+        return launch_mask_m<128>(p, kind, n_qt, st);
     default:
-        return launch_kind_m<256>(p, kind, n_qt, st);
+        return launch_mask_m<256>(p, kind, n_qt, st);
     }
 }
 

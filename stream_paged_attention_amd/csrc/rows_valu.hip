@@ -212,14 +212,16 @@ __device__ __forceinline__ float groups_max(float x)
 }
 
 // Fold one K/V tile.  key0 is the lane's first key.  With MASKED, key
-// key0 + KPS*j counts for query vector v only below lim[v] (causal limit and
-// split end) and then adds exactly nothing, not even a NaN from its value.
-template <int D, int QT, bool MASKED>
+// key0 + KPS*j counts for query vector v only below lim[v] (mask limit and
+// split end) and, under a tree mask, when it is the row's or an ancestor's
+// (row_sees); a key that does not
+// count adds exactly nothing, not even a NaN from its value.
+template <int D, int QT, bool MASKED, int MASK>
 __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][Geo<D, QT>::W],
                                           const uint32_t (&vb)[Geo<D, QT>::NS][Geo<D, QT>::W],
                                           const uint32_t (&qr)[QT][Geo<D, QT>::W], float c,
                                           float lazy, State<D, QT> &st, int key0,
-                                          const int (&lim)[QT])
+                                          const int (&lim)[QT], int tb, const uint64_t (&anc)[QT])
 {
     using G = Geo<D, QT>;
     constexpr int NS = G::NS, W = G::W, DPL = G::DPL, KPS = G::KPS;
@@ -248,7 +250,8 @@ __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][G
             // the smallest counted score: a -inf score gives p = 0, so it
             // has to be recorded apart (NaN rule)
             if constexpr (MASKED) {
-                const bool vis = key0 + KPS * j < lim[v];
+                const int key = key0 + KPS * j;
+                const bool vis = row_sees<MASK>(key, lim[v], tb, anc[v]);
                 st.lo[v] = vmin(st.lo[v], vis ? s[v][j] : INFINITY);
                 s[v][j] = vis ? s[v][j] : -INFINITY;
             } else {
@@ -303,7 +306,8 @@ __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][G
             if constexpr (MASKED) {
                 // a key this query vector may not see has p = 0; its value is
                 // replaced by 0 too, so a NaN there cannot leak in
-                const bool vis = key0 + KPS * j < lim[v];
+                const int key = key0 + KPS * j;
+                const bool vis = row_sees<MASK>(key, lim[v], tb, anc[v]);
 #pragma unroll
                 for (int d = 0; d < DPL; ++d)
                     st.o[v][d] = fmaf(s[v][j], vis ? vf[d] : 0.0f, st.o[v][d]);
@@ -316,7 +320,7 @@ __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][G
     }
 }
 
-template <int D, int KIND, int QT>
+template <int D, int KIND, int QT, int MASK>
 __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
 {
     using G = Geo<D, QT>;
@@ -360,7 +364,8 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
 
     // ---- per-segment checks (identical in every work item of the segment)
     const bool rows_ok = s.n_rows >= 1 && s.n_rows <= s.key_count && s.row_offset >= 0 &&
-                         (int64_t)s.row_offset + s.n_rows <= p.total_rows;
+                         (int64_t)s.row_offset + s.n_rows <= p.total_rows &&
+                         (MASK != TF_MASK_TREE || s.n_rows <= 64);
     if (!rows_ok) {
         // no row of this segment can be addressed safely: report and write nothing
         if (threadIdx.x == 0 && g == 0 && t == 0)
@@ -407,6 +412,8 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
         // ---- query vectors of this pass: v -> (row r, head h)
         uint32_t qr[QT][W];
         int lim[QT];
+        uint64_t anc[QT];
+        int tb = INT32_MAX;   // the segment's first new key under a tree mask
         State<D, QT> st;
 #pragma unroll
         for (int v = 0; v < QT; ++v) {
@@ -425,15 +432,20 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
                 load_row<D, QT>(qr[v], reinterpret_cast<const char *>(p.q) +
                                            ((size_t)(s.row_offset + r) * p.hq + h) * (D * 2),
                                 (uint32_t)(sl * (G::DPL == 4 ? 8 : 16)));
-                lim[v] = min(s.key_count - s.n_rows + r + 1, k_end);
+                const RowVis rv = row_vis<MASK>(p, s.key_count, s.n_rows, r, s.row_offset, k_end);
+                lim[v] = rv.lim;
+                anc[v] = rv.anc;
+                tb = rv.tb;
             } else {
 #pragma unroll
                 for (int w = 0; w < W; ++w)
                     qr[v][w] = 0u;
                 lim[v] = 0;
+                anc[v] = 0;
             }
         }
-        int lim_min = lim[0];
+        // keys below lim_min count for every query vector of the pass
+        int lim_min = min(lim[0], tb);
 #pragma unroll
         for (int v = 1; v < QT; ++v)
             if (qt0 + v < nq)
@@ -501,7 +513,7 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
         // take the loads of tile i + CH.  Loads past the last full tile
         // repeat it (an L2 hit, never waited for: the barriers below order
         // LDS only) so that every wait before a fold is an exact count in
-        // issue order.  The masked tail (split end, causal rows) is folded
+        // issue order.  The masked tail (split end, causal rows, a tree's block) is folded
         // one tile at a time by its own loop.
         const int n_full = max(0, min(n_tiles, (lim_min - k0) / TK));
         const int my_full = n_full > wave ? (n_full - wave + kWaves - 1) / kWaves : 0;
@@ -519,7 +531,7 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
                 for (int u = 0; u < CH; ++u) {
                     const int i = i0 + u;
                     if (i < b1)
-                        fold_tile<D, QT, false>(kb[u], vb[u], qr, c, lazy, st, tile_key0(i) + kg, lim);
+                        fold_tile<D, QT, false, MASK>(kb[u], vb[u], qr, c, lazy, st, tile_key0(i) + kg, lim, tb, anc);
                     load_tile(kb[u], vb[u], min(i + CH, b1 - 1));
                 }
             }
@@ -529,7 +541,7 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
                 load_pids(i & ~63);
             uint32_t kb[NS][W], vb[NS][W];
             load_tile(kb, vb, i);
-            fold_tile<D, QT, true>(kb, vb, qr, c, lazy, st, tile_key0(i) + kg, lim);
+            fold_tile<D, QT, true, MASK>(kb, vb, qr, c, lazy, st, tile_key0(i) + kg, lim, tb, anc);
         }
         if (page_bad) {
             if (lane == 0)
@@ -641,7 +653,12 @@ static_assert(kMfmaMinQ <= 4, "the decode kernel is launched for 4 query vectors
 template <int D, int KIND>
 hipError_t launch_qt(const RowsParams &p, dim3 grid, hipStream_t st)
 {
-    hipLaunchKernelGGL((rows_valu_kernel<D, KIND, 4>), grid, dim3(kThreads), 0, st, p);
+    if (p.mask == TF_MASK_TREE)
+        hipLaunchKernelGGL((rows_valu_kernel<D, KIND, 4, TF_MASK_TREE>), grid, dim3(kThreads), 0, st, p);
+    else if (p.mask == TF_MASK_FULL)
+        hipLaunchKernelGGL((rows_valu_kernel<D, KIND, 4, TF_MASK_FULL>), grid, dim3(kThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((rows_valu_kernel<D, KIND, 4, TF_MASK_CAUSAL>), grid, dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 

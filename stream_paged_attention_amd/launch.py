@@ -50,6 +50,9 @@ class DeviceWorkload:
         self.q = _dev(w.q, self.device)
         self.out = torch.zeros(w.q.shape, dtype=torch.int16, device=self.device)
         self.err = torch.zeros(1, dtype=torch.int32, device=self.device)
+        self.mask = binding.MASK_CODE[w.mask]
+        self.tree = (_dev(np.ascontiguousarray(w.tree, dtype=np.uint64).view(np.int64), self.device)
+                     if w.mask == "tree" else None)
         self.copies = copies
         self.k_store: List[List[torch.Tensor]] = []
         self.v_store: List[List[torch.Tensor]] = []
@@ -126,6 +129,8 @@ class DeviceWorkload:
         a.pool_pages = w.pool_pages if w.kind == "paged" else 0
         a.split_keys = self.split_keys
         a.scale = w.scale
+        a.mask = self.mask
+        a.tree = self.tree.data_ptr() if self.tree is not None else None
         a.segs = self.tables[copy].data_ptr()
         a.q = self.q.data_ptr()
         a.out = self.out.data_ptr()
@@ -174,6 +179,8 @@ class DeviceWorkload:
             a.min_rows = s.n_rows
             a.q = self.q.data_ptr() + s.row_offset * row_bytes
             a.out = out.data_ptr() + s.row_offset * row_bytes
+            if self.tree is not None:
+                a.tree = self.tree.data_ptr() + 8 * s.row_offset
             part = None
             if self.split_keys > 0:
                 rc, nbytes = binding.tf_plan_partials(one, w.n_q_heads, w.head_dim,

@@ -97,6 +97,8 @@ class Workload:
     store_v: Optional[List[np.ndarray]] = None
     logits: Optional[np.ndarray] = None   # uint16 [rows][vocab]
     notes: str = ""
+    mask: str = "causal"                  # "causal", "full" or "tree"
+    tree: Optional[np.ndarray] = None     # tree: uint64 ancestor mask per packed row
 
     @property
     def total_rows(self) -> int:
@@ -282,6 +284,44 @@ def make_workload(name: str, kind: str, n_q_heads: int, n_kv_heads: int, head_di
     else:
         raise ValueError(kind)
     return w
+
+
+def random_parents(rng: np.random.Generator, n: int, chain: bool = False) -> np.ndarray:
+    """A draft tree over a segment's n rows: parent[r] < r, or -1 for a row
+    that hangs off the context alone.  Row 0 is the root; ``chain`` gives the
+    degenerate tree parent[r] = r - 1."""
+    if chain:
+        return np.arange(-1, n - 1, dtype=np.int64)
+    par = np.full(n, -1, dtype=np.int64)
+    for r in range(1, n):
+        par[r] = int(rng.integers(0, r))
+    return par
+
+
+def ancestor_masks(parents: Sequence[int]) -> np.ndarray:
+    """The tree mask format the library takes: for each row, bit j set when
+    row j lies on its path to the root (the row itself not included)."""
+    n = len(parents)
+    assert n <= 64
+    out = np.zeros(n, dtype=np.uint64)
+    for r in range(n):
+        bits, a = 0, int(parents[r])
+        while a >= 0:
+            assert a < r
+            bits |= 1 << a
+            a = int(parents[a])
+        out[r] = np.uint64(bits)
+    return out
+
+
+def with_trees(w: Workload, seed: int, chain: bool = False) -> Workload:
+    """The same workload under a tree mask, one drawn tree per segment."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    tree = np.zeros(w.total_rows, dtype=np.uint64)
+    for s in w.segments:
+        tree[s.row_offset:s.row_offset + s.n_rows] = ancestor_masks(
+            random_parents(rng, s.n_rows, chain))
+    return dataclasses.replace(w, mask="tree", tree=tree)
 
 
 def normal_logits(rng: np.random.Generator, rows: int, vocab: int) -> np.ndarray:

@@ -25,14 +25,32 @@ def causal_mask(n, kc):
     return j < (kc - n + r + 1)
 
 
-def sdpa(n_rows, kcs, q, kl, vl, hq, hkv, d):
-    """torch float64 SDPA per segment, grouped-query mode, causal-count mask."""
+def full_mask(n, kc):
+    return np.ones((n, kc), dtype=bool)
+
+
+def tree_mask(n, kc, parents):
+    """Context keys, the row's own key, and its ancestors' keys, found by
+    walking the parent links."""
+    m = np.zeros((n, kc), dtype=bool)
+    m[:, :kc - n] = True
+    for r in range(n):
+        a = r
+        while a >= 0:
+            m[r, kc - n + a] = True
+            a = int(parents[a])
+    return m
+
+
+def sdpa(n_rows, kcs, q, kl, vl, hq, hkv, d, masks=None):
+    """torch float64 SDPA per segment, grouped-query mode, with a boolean mask
+    per segment (the causal-count mask unless ``masks`` gives one)."""
     outs, off = [], 0
-    for n, kc, k, v in zip(n_rows, kcs, kl, vl):
+    for i, (n, kc, k, v) in enumerate(zip(n_rows, kcs, kl, vl)):
         qq = torch.from_numpy(f64(q[off:off + n])).permute(1, 0, 2)[None]
         kk = torch.from_numpy(f64(k)).permute(1, 0, 2)[None]
         vv = torch.from_numpy(f64(v)).permute(1, 0, 2)[None]
-        mask = torch.from_numpy(causal_mask(n, kc))
+        mask = torch.from_numpy(causal_mask(n, kc) if masks is None else masks[i])
         o = F.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask,
                                            scale=1.0 / math.sqrt(d), enable_gqa=hq != hkv)
         outs.append(o[0].permute(1, 0, 2).numpy())
@@ -81,15 +99,36 @@ SDPA_CASES = [
     (7, 4, 1, 8, [(3, 33)], 400.0),   # scores far past exp()'s range: needs the max subtraction
 ]
 
+# Cases for the full and tree masks: blocks of several rows, some with no
+# context (key count == rows), some with a long one.
+MASK_CASES = [
+    (51, 2, 1, 4, [(4, 4), (1, 6)], 1.0),
+    (52, 4, 2, 8, [(9, 40), (3, 3), (6, 7)], 1.0),
+    (53, 8, 2, 16, [(16, 100)], 1.0),
+    (54, 4, 1, 8, [(5, 20)], 300.0),
+]
 
-def check_attention(attn_fn, cases=SDPA_CASES, tol=1e-12):
-    """Return the worst |oracle - sdpa| over the cases."""
+
+def check_attention(attn_fn, cases=SDPA_CASES, tol=1e-12, mask="causal"):
+    """Return the worst |oracle - sdpa| over the cases, under the causal, full
+    or tree mask (trees: parents drawn per segment, passed to the oracle as
+    ancestor bit masks and to torch as boolean masks)."""
     worst = 0.0
     for seed, hq, hkv, d, segs, qs in cases:
         n_rows, kcs, q, kl, vl = random_case(seed, hq, hkv, d, segs, qs)
+        kw = {}
+        masks = None
+        if mask == "full":
+            kw = dict(mask="full")
+            masks = [full_mask(n, kc) for n, kc in zip(n_rows, kcs)]
+        elif mask == "tree":
+            rng = np.random.Generator(np.random.PCG64(seed + 1000))
+            parents = [synth.random_parents(rng, n) for n in n_rows]
+            kw = dict(mask="tree", tree=np.concatenate([synth.ancestor_masks(p) for p in parents]))
+            masks = [tree_mask(n, kc, p) for n, kc, p in zip(n_rows, kcs, parents)]
         got = attn_fn(n_rows, kcs, q, kl, vl, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
-                      scale=1.0 / math.sqrt(d))
-        ref = sdpa(n_rows, kcs, q, kl, vl, hq, hkv, d)
+                      scale=1.0 / math.sqrt(d), **kw)
+        ref = sdpa(n_rows, kcs, q, kl, vl, hq, hkv, d, masks)
         if not np.all(np.isfinite(got)):
             return math.inf
         worst = max(worst, float(np.max(np.abs(got - ref))))

@@ -108,6 +108,8 @@ def _args(**kw):
     a.out = kw.get("out", fake)
     a.partials = kw.get("partials", None)
     a.partials_bytes = kw.get("partials_bytes", 0)
+    a.mask = kw.get("mask", binding.TF_MASK_CAUSAL)
+    a.tree = kw.get("tree", None)
     return a
 
 
@@ -130,10 +132,27 @@ def _args(**kw):
     (dict(scale=-0.1), binding.TF_E_INVALID),
     (dict(scale=float("inf")), binding.TF_E_INVALID),
     (dict(scale=float("nan")), binding.TF_E_INVALID),
+    (dict(mask=3), binding.TF_E_INVALID),
+    (dict(mask=-1), binding.TF_E_INVALID),
+    (dict(mask=binding.TF_MASK_TREE), binding.TF_E_INVALID),                    # tree masks missing
+    (dict(mask=binding.TF_MASK_TREE, tree=0x50004), binding.TF_E_INVALID),      # misaligned
+    (dict(mask=binding.TF_MASK_TREE, tree=0x50000, max_rows=65, max_keys=100),
+     binding.TF_E_INVALID),                                                     # more than 64 rows
 ])
 def test_rows_refuses_bad_scalars_without_launching(kw, rc):
     # stream 0 and fake pointers: a refused call must return before any launch
     assert binding.tf_attn_rows(_args(**kw), 0) == rc
+
+
+def test_tree_mask_limits_on_the_host_table():
+    t = _host_table([(4, 0, 0, 64, 100), (4, 0, 64, 1, 40)])
+    a = _args(total_rows=65, n_segments=2, max_rows=64, mask=binding.TF_MASK_TREE, tree=0x50000)
+    assert binding.tf_check_segments(a, t) == binding.TF_OK
+    big = _host_table([(4, 0, 0, 65, 100)])
+    a = _args(total_rows=65, max_rows=65, mask=binding.TF_MASK_TREE, tree=0x50000)
+    assert binding.tf_check_segments(a, big) == binding.TF_E_INVALID
+    a.mask = binding.TF_MASK_FULL
+    assert binding.tf_check_segments(a, big) == binding.TF_OK
 
 
 def test_merge_needs_split_partials():

@@ -17,14 +17,24 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 ATTN_CONTROLS = [
     ("gqa groups interleaved", "const int g = t->head / group;", "const int g = t->head % hkv;"),
     ("scale dropped", "acc *= scale;", ";"),
-    ("causal count off by one", "key_count[s] - n_rows[s] + r + 1", "key_count[s] - n_rows[s] + r"),
+    ("causal count off by one", "return j <= first_new + t->row;", "return j < first_new + t->row;"),
     ("max subtraction sign", "const double p = exp(s[j] - m);", "const double p = exp(m - s[j]);"),
-    ("last visible key dropped from P.V",
-     "for (int j = 0; j < t->visible; ++j) {\n                const double p",
-     "for (int j = 0; j + 1 < t->visible; ++j) {\n                const double p"),
+    ("last key dropped from P.V",
+     "for (int j = 0; j < t->key_count; ++j) {\n                if (!sees(t, j))\n                    continue;\n                const double p",
+     "for (int j = 0; j + 1 < t->key_count; ++j) {\n                if (!sees(t, j))\n                    continue;\n                const double p"),
     ("k dims reversed", "acc += qd[x] * bf16_value(kr[x]);", "acc += qd[x] * bf16_value(kr[d - 1 - x]);"),
     ("v read from kv head 0", "const uint16_t *vr = vs + ((int64_t)j * hkv + g) * d;\n                l += p;",
      "const uint16_t *vr = vs + ((int64_t)j * hkv) * d;\n                l += p;"),
+]
+FULL_CONTROLS = [
+    ("full read as causal", "case MASK_FULL:\n        return 1;", "case MASK_FULL:\n        return j <= first_new + t->row;"),
+    ("full drops the newest key", "case MASK_FULL:\n        return 1;", "case MASK_FULL:\n        return j + 1 < t->key_count;"),
+]
+TREE_CONTROLS = [
+    ("tree bit off by one", "(t->anc >> (j - first_new)) & 1u", "(t->anc >> (j - first_new + 1)) & 1u"),
+    ("tree row misses its own key", "if (j < first_new || j == first_new + t->row)", "if (j < first_new)"),
+    ("tree context dropped", "if (j < first_new || j == first_new + t->row)", "if (j == first_new + t->row)"),
+    ("tree masks read from the segment's first row", "tree[row_offset[s] + r]", "tree[row_offset[s]]"),
 ]
 ARGMAX_CONTROLS = [
     ("ties to the highest id", "if (i == 0 || key > best_key)", "if (i == 0 || key >= best_key)"),
@@ -78,6 +88,20 @@ def test_unedited_source_is_green(tmp_path):
 @pytest.mark.parametrize("name,old,new", ATTN_CONTROLS, ids=[c[0] for c in ATTN_CONTROLS])
 def test_attention_control_goes_red(tmp_path, name, old, new):
     assert _attention_red(_build_variant(tmp_path, old, new)), name
+
+
+@pytest.mark.parametrize("name,old,new", FULL_CONTROLS, ids=[c[0] for c in FULL_CONTROLS])
+def test_full_control_goes_red(tmp_path, name, old, new):
+    lib = _build_variant(tmp_path, old, new)
+    cases = pins.SDPA_CASES + pins.MASK_CASES
+    assert pins.check_attention(functools.partial(oracle.attn, lib=lib), cases, mask="full") > 1e-9, name
+
+
+@pytest.mark.parametrize("name,old,new", TREE_CONTROLS, ids=[c[0] for c in TREE_CONTROLS])
+def test_tree_control_goes_red(tmp_path, name, old, new):
+    lib = _build_variant(tmp_path, old, new)
+    cases = pins.SDPA_CASES + pins.MASK_CASES
+    assert pins.check_attention(functools.partial(oracle.attn, lib=lib), cases, mask="tree") > 1e-9, name
 
 
 @pytest.mark.parametrize("name,old,new", ARGMAX_CONTROLS, ids=[c[0] for c in ARGMAX_CONTROLS])

@@ -120,6 +120,103 @@ def test_partials_hold_the_split_max_and_sums():
         np.testing.assert_allclose(o[0, 0, t], p @ vv[t * split:(t + 1) * split], atol=1e-12)
 
 
+# --------------------------------------------------------------------------- full and tree masks
+
+def test_full_mask_matches_torch_sdpa_float64():
+    # FULL: every row of a block sees every key of its stream.
+    assert pins.check_attention(oracle.attn, pins.SDPA_CASES + pins.MASK_CASES, mask="full") <= 1e-12
+
+
+def test_tree_mask_matches_torch_sdpa_float64():
+    # tree: context, the row's own key and its ancestors' keys.
+    assert pins.check_attention(oracle.attn, pins.SDPA_CASES + pins.MASK_CASES, mask="tree") <= 1e-12
+
+
+def test_full_rows_equal_one_row_segments_over_all_keys():
+    hq, hkv, d, n, kc = 4, 2, 8, 6, 19
+    n_rows, kcs, q, kl, vl = pins.random_case(41, hq, hkv, d, [(n, kc)])
+    kw = dict(n_q_heads=hq, n_kv_heads=hkv, head_dim=d, scale=1 / math.sqrt(d))
+    a = oracle.attn(n_rows, kcs, q, kl, vl, mask="full", **kw)
+    b = oracle.attn([1] * n, [kc] * n, q, kl * n, vl * n, **kw)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_full_mask_ignores_key_order():
+    hq, hkv, d, n, kc = 4, 2, 8, 5, 31
+    n_rows, kcs, q, kl, vl = pins.random_case(42, hq, hkv, d, [(n, kc)])
+    perm = np.random.Generator(np.random.PCG64(42)).permutation(kc)
+    kw = dict(n_q_heads=hq, n_kv_heads=hkv, head_dim=d, scale=1 / math.sqrt(d), mask="full")
+    a = oracle.attn(n_rows, kcs, q, kl, vl, **kw)
+    b = oracle.attn(n_rows, kcs, q, [kl[0][perm]], [vl[0][perm]], **kw)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+def test_chain_tree_equals_causal():
+    # A tree whose rows form one chain is the causal count.
+    hq, hkv, d = 4, 2, 8
+    segs = [(7, 30), (1, 5), (3, 3)]
+    n_rows, kcs, q, kl, vl = pins.random_case(43, hq, hkv, d, segs)
+    kw = dict(n_q_heads=hq, n_kv_heads=hkv, head_dim=d, scale=1 / math.sqrt(d))
+    tree = np.concatenate([synth.ancestor_masks(np.arange(-1, n - 1)) for n in n_rows])
+    a = oracle.attn(n_rows, kcs, q, kl, vl, mask="tree", tree=tree, **kw)
+    b = oracle.attn(n_rows, kcs, q, kl, vl, **kw)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_tree_node_equals_its_chain():
+    # Each node equals the last row of a causal segment holding the context,
+    # its ancestors and itself, in key order.
+    hq, hkv, d, n, kc = 4, 2, 8, 12, 40
+    n_rows, kcs, q, kl, vl = pins.random_case(44, hq, hkv, d, [(n, kc)])
+    par = synth.random_parents(np.random.Generator(np.random.PCG64(44)), n)
+    kw = dict(n_q_heads=hq, n_kv_heads=hkv, head_dim=d, scale=1 / math.sqrt(d))
+    a = oracle.attn(n_rows, kcs, q, kl, vl, mask="tree", tree=synth.ancestor_masks(par), **kw)
+    for r in range(n):
+        path, x = [], r
+        while x >= 0:
+            path.append(x)
+            x = int(par[x])
+        keys = list(range(kc - n)) + [kc - n + x for x in sorted(path)]
+        b = oracle.attn([1], [len(keys)], q[r:r + 1], [kl[0][keys]], [vl[0][keys]], **kw)
+        np.testing.assert_array_equal(a[r], b[0])
+
+
+@pytest.mark.parametrize("mask", ["full", "tree"])
+def test_masked_split_and_merge_equal_unsplit(mask):
+    hq, hkv, d, split = 4, 2, 8, 5
+    segs = [(9, 40), (4, 4), (1, 13)]
+    n_rows, kcs, q, kl, vl = pins.random_case(45, hq, hkv, d, segs)
+    kw = dict(n_q_heads=hq, n_kv_heads=hkv, head_dim=d, scale=1 / math.sqrt(d), mask=mask)
+    if mask == "tree":
+        rng = np.random.Generator(np.random.PCG64(45))
+        kw["tree"] = np.concatenate([synth.ancestor_masks(synth.random_parents(rng, n))
+                                     for n in n_rows])
+    full = oracle.attn(n_rows, kcs, q, kl, vl, **kw)
+    m, l, o = oracle.attn_partials(n_rows, kcs, q, kl, vl, split=split, **kw)
+    np.testing.assert_allclose(oracle.merge(m, l, o), full, rtol=0, atol=1e-12)
+
+
+def test_full_mask_reads_keys_past_the_causal_limit():
+    hq, hkv, d, n, kc = 4, 2, 8, 3, 12
+    n_rows, kcs, q, kl, vl = pins.random_case(46, hq, hkv, d, [(n, kc)])
+    kl[0][kc - 1, :, 0] = synth.BF16_NAN
+    out = oracle.attn(n_rows, kcs, q, kl, vl, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                      scale=1 / math.sqrt(d), mask="full")
+    assert np.isnan(out).all()
+
+
+def test_tree_never_reads_a_sibling_key():
+    hq, hkv, d, n, kc = 4, 2, 8, 4, 10
+    n_rows, kcs, q, kl, vl = pins.random_case(47, hq, hkv, d, [(n, kc)])
+    par = np.array([-1, 0, 0, 1])        # rows 1 and 2 are siblings; 3 under 1
+    kl[0][kc - n + 2] = synth.BF16_NAN   # row 2's key
+    vl[0][kc - n + 2] = synth.BF16_NAN
+    out = oracle.attn(n_rows, kcs, q, kl, vl, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                      scale=1 / math.sqrt(d), mask="tree", tree=synth.ancestor_masks(par))
+    assert np.isnan(out[2]).all()
+    assert np.isfinite(out[[0, 1, 3]]).all()
+
+
 # --------------------------------------------------------------------------- NaN rule
 
 def _nan_case():
