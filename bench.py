@@ -125,6 +125,75 @@ def bench_kv_put(args, w, dw, copies, stream) -> int:
     return 0
 
 
+def bench_state(args) -> int:
+    """tf_state_save and tf_state_restore of a kept state: ten layers' K and V
+    at positions [0, 6243) (8 KV heads x D 64, 512-position pages of a
+    shuffled page list), alternating between two disjoint page lists and two
+    state buffers so that the working set exceeds the last-level cache.  Bytes
+    per call = what is read plus what is written."""
+    import ctypes
+    import numpy as np
+    import torch
+    from stream_paged_attention_amd import binding
+    dev = torch.device("cuda:0")
+    layers, hkv, d, page, at, pool_pages = 10, 8, 64, 512, 6243, 32
+    n_state = -(-at // page)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6243)
+    rnd = lambda *shape: torch.randint(-32768, 32767, shape, dtype=torch.int16, device=dev, generator=gen)
+    pools = [(rnd(pool_pages, hkv, page, d), rnd(pool_pages, hkv, page, d)) for _ in range(layers)]
+    states = [[(rnd(n_state, hkv, page, d), rnd(n_state, hkv, page, d)) for _ in range(layers)] for _ in range(2)]
+    perm = np.random.Generator(np.random.PCG64(6243)).permutation(pool_pages).astype(np.int32)
+    page_lists = [torch.from_numpy(perm[i * n_state:(i + 1) * n_state].copy()).to(dev) for i in range(2)]
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    keep = []
+    argl = []
+    for c in range(2):
+        table = (binding.tf_state_layer * layers)()
+        for i in range(layers):
+            table[i].pool_k, table[i].pool_v = pools[i][0].data_ptr(), pools[i][1].data_ptr()
+            table[i].state_k, table[i].state_v = states[c][i][0].data_ptr(), states[c][i][1].data_ptr()
+        raw = bytes(ctypes.string_at(ctypes.addressof(table), ctypes.sizeof(table)))
+        t = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(dev)
+        keep.append(t)
+        a = binding.tf_state_args()
+        a.n_layers, a.n_kv_heads, a.head_dim, a.page_size, a.pool_pages = layers, hkv, d, page, pool_pages
+        a.at, a.n_pages, a.pages, a.layers, a.err = at, n_state, page_lists[c].data_ptr(), t.data_ptr(), err.data_ptr()
+        argl.append(a)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    nbytes = 2 * layers * 2 * at * hkv * d * 2
+    res = {}
+    for name, fn in (("save", binding.tf_state_save), ("restore", binding.tf_state_restore)):
+        for i in range(args.warmup):
+            assert fn(argl[i % 2], st) == 0
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(args.steps):
+            fn(argl[i % 2], st)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+        res[name] = (ms, nbytes / (ms * 1e-3) / 1e9)
+    assert int(err.item()) == 0
+    gbps = res["save"][1]
+    print(json.dumps({
+        "metric": "kept-state copy GB/s (read + written), save", "value": round(gbps, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["save"][0], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "kept state of a 6,243-position history: 10 layers' K and V, 8 KV heads x D 64, "
+                               "512-position pages of a shuffled page list",
+                   "bytes_per_call": nbytes, "restore_ms": round(res["restore"][0], 5),
+                   "restore_gbps": round(res["restore"][1], 2)},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 3), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "tf_state_save (state_copy_kernel)",
+                     "restore_frac": round(res["restore"][1] / HBM_PEAK_GBPS, 4)},
+    }), flush=True)
+    return 0
+
+
 def synth_title(n: int) -> str:
     from stream_paged_attention_amd import synth
     return synth.CONFIG_TITLES[n]
@@ -141,8 +210,9 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kernel-only", action="store_true",
                     help="time only tf_attn_rows launches (for profiler runs)")
-    ap.add_argument("--op", choices=["attn", "kv_put"], default="attn",
-                    help="kv_put: time tf_kv_put of the workload's round rows instead")
+    ap.add_argument("--op", choices=["attn", "kv_put", "state"], default="attn",
+                    help="kv_put: time tf_kv_put of the workload's round rows instead; "
+                         "state: time tf_state_save / tf_state_restore of a kept state")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run 20 plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -168,6 +238,8 @@ def main() -> int:
         print(json.dumps({"copy_bytes": x.numel(), "copies": 20}), flush=True)
         return 0
     binding.load()
+    if args.op == "state":
+        return bench_state(args)
     w = synth.make_config(args.config)
     pool_bytes = (w.pool_k.nbytes * 2 if w.pool_k is not None
                   else sum(x.nbytes for x in w.store_k) * 2)

@@ -97,7 +97,8 @@ enum {
     TF_ERR_BAD_ROWS = 4,   /* n_rows < 1, n_rows > key_count, rows outside [0, total_rows), or
                               n_rows > 64 under TF_MASK_TREE                                   */
     TF_ERR_BAD_RING = 8,   /* ring first outside [0, capacity)                                   */
-    TF_ERR_PARTIALS = 16   /* the segment's partial records fall outside the workspace           */
+    TF_ERR_PARTIALS = 16,  /* the segment's partial records fall outside the workspace           */
+    TF_ERR_BAD_LAYER = 32  /* tf_state_*: a layer's pointer is null or not 16-byte aligned       */
 };
 
 /*
@@ -243,6 +244,50 @@ typedef struct tf_put_args {
 } tf_put_args;
 
 int tf_kv_put(const tf_put_args *a, hipStream_t stream);
+
+/*
+ * Kept state copy (TensorFold PR #1503, the prompt-cache commit of the
+ * lfm2_moe pool: a kept state holds every attention layer's keys and values
+ * at positions [0, at), copied run by run with whole pages coalesced, and is
+ * restored into the leased pages of the stream that resumes it).
+ *
+ * tf_state_save copies positions [0, at) of every layer's K and V from the
+ * stream's pool pages into the layer's state buffers; tf_state_restore copies
+ * them back into another page list (the new stream's pages).  Pool pages are
+ * [pool_pages][n_kv_heads][page_size][head_dim] bf16 (the PAGED layout of
+ * tf_kv_kind); a state buffer has the same shape with the stream's logical
+ * pages in order, [ceil(at / page_size)][n_kv_heads][page_size][head_dim]:
+ * state page i holds the rows of logical page i, so whole pages copy as
+ * units and the last page copies only its first at - (pages - 1) * page_size
+ * rows.  Rows at or past `at` are never written: not in the state (save),
+ * not in the pool (restore).  Page ids outside [0, pool_pages) set
+ * TF_ERR_BAD_PAGE and that page is skipped; a null or misaligned layer
+ * pointer sets TF_ERR_BAD_LAYER and that layer is skipped.  One launch
+ * covers every layer.  Returns TF_OK, TF_E_INVALID, TF_E_UNSUPPORTED or
+ * TF_E_PAST_PAGES (at > n_pages * page_size), nothing launched on an error.
+ */
+typedef struct tf_state_layer {
+    void *pool_k;             /* device bf16 pool of the layer's keys                        */
+    void *pool_v;             /* device bf16 pool of the layer's values                      */
+    void *state_k;            /* device bf16 state buffer of the layer's keys                */
+    void *state_v;            /* device bf16 state buffer of the layer's values              */
+} tf_state_layer;
+
+typedef struct tf_state_args {
+    int32_t n_layers;         /* >= 0                                                        */
+    int32_t n_kv_heads;       /* >= 1                                                        */
+    int32_t head_dim;         /* 64, 128 or 256                                              */
+    int32_t page_size;        /* positions per page (power of two, 32..1024)                 */
+    int32_t pool_pages;       /* pages in each pool (page ids are checked against it)        */
+    int32_t at;               /* positions [0, at) are copied; >= 0                          */
+    int32_t n_pages;          /* entries of pages[]                                          */
+    const int32_t *pages;     /* device: the stream's logical page -> pool page id           */
+    const tf_state_layer *layers; /* device: n_layers entries, pointers 16-byte aligned      */
+    int32_t *err;             /* device int32 error word, or NULL                            */
+} tf_state_args;
+
+int tf_state_save(const tf_state_args *a, hipStream_t stream);
+int tf_state_restore(const tf_state_args *a, hipStream_t stream);
 
 /* Workspace bytes tf_argmax needs for n_rows rows of vocab logits. */
 size_t tf_argmax_workspace_bytes(int32_t n_rows, int32_t vocab);

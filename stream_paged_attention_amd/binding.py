@@ -31,9 +31,11 @@ TF_ERR_BAD_PAGE = 2
 TF_ERR_BAD_ROWS = 4
 TF_ERR_BAD_RING = 8
 TF_ERR_PARTIALS = 16
+TF_ERR_BAD_LAYER = 32
 
 EXPORTS = ("tf_attn_rows", "tf_attn_merge", "tf_argmax", "tf_argmax_workspace_bytes",
-           "tf_kv_put", "tf_plan_partials", "tf_check_segments", "tf_strerror")
+           "tf_kv_put", "tf_state_save", "tf_state_restore", "tf_plan_partials",
+           "tf_check_segments", "tf_strerror")
 
 
 class tf_segment(ctypes.Structure):
@@ -67,6 +69,19 @@ class tf_put_args(ctypes.Structure):
                 ("err", ctypes.c_void_p)]
 
 
+class tf_state_layer(ctypes.Structure):
+    _fields_ = [("pool_k", ctypes.c_void_p), ("pool_v", ctypes.c_void_p),
+                ("state_k", ctypes.c_void_p), ("state_v", ctypes.c_void_p)]
+
+
+class tf_state_args(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("pool_pages", ctypes.c_int32), ("at", ctypes.c_int32),
+                ("n_pages", ctypes.c_int32), ("pages", ctypes.c_void_p),
+                ("layers", ctypes.c_void_p), ("err", ctypes.c_void_p)]
+
+
 assert ctypes.sizeof(tf_segment) == 48
 
 _lib = None
@@ -92,6 +107,9 @@ def load(path: str = LIB_PATH):
     lib.tf_argmax_workspace_bytes.argtypes = [i32, i32]
     lib.tf_kv_put.restype = ctypes.c_int
     lib.tf_kv_put.argtypes = [ctypes.POINTER(tf_put_args), vp]
+    for name in ("tf_state_save", "tf_state_restore"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = [ctypes.POINTER(tf_state_args), vp]
     lib.tf_plan_partials.restype = ctypes.c_int
     lib.tf_plan_partials.argtypes = [ctypes.POINTER(tf_segment), i32, i32, i32, i32,
                                      ctypes.POINTER(sz)]
@@ -124,6 +142,14 @@ def tf_argmax_workspace_bytes(n_rows: int, vocab: int, lib=None) -> int:
 
 def tf_kv_put(args: tf_put_args, stream: int, lib=None) -> int:
     return (lib or load()).tf_kv_put(ctypes.byref(args), ctypes.c_void_p(stream))
+
+
+def tf_state_save(args: tf_state_args, stream: int, lib=None) -> int:
+    return (lib or load()).tf_state_save(ctypes.byref(args), ctypes.c_void_p(stream))
+
+
+def tf_state_restore(args: tf_state_args, stream: int, lib=None) -> int:
+    return (lib or load()).tf_state_restore(ctypes.byref(args), ctypes.c_void_p(stream))
 
 
 def tf_plan_partials(segs, n_q_heads: int, head_dim: int, split_keys: int, lib=None):

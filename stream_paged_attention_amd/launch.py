@@ -256,3 +256,69 @@ def argmax(logits: np.ndarray, device="cuda:0", vocab: Optional[int] = None):
                             ws.data_ptr(), nbytes, st), "tf_argmax")
     torch.cuda.synchronize(dev)
     return ids.cpu().numpy(), flags.cpu().numpy()
+
+
+class DeviceState:
+    """Device copies of per-layer pools and kept-state buffers, and the
+    tf_state_save / tf_state_restore calls on them.
+
+    ``pools`` and ``states`` are lists of (K, V) host arrays per layer
+    (bf16 bits, [pages][Hkv][P][D]); ``pages`` is the stream's page list.
+    """
+
+    def __init__(self, pools, states, pages, at: int, device="cuda:0"):
+        self.device = torch.device(device)
+        self.pk = [_dev(k, self.device) for k, _ in pools]
+        self.pv = [_dev(v, self.device) for _, v in pools]
+        self.sk = [_dev(k, self.device) for k, _ in states]
+        self.sv = [_dev(v, self.device) for _, v in states]
+        self.pool_pages, self.hkv, self.page_size, self.head_dim = pools[0][0].shape
+        self.at = at
+        self.err = torch.zeros(1, dtype=torch.int32, device=self.device)
+        self.set_pages(pages)
+        table = (binding.tf_state_layer * len(pools))()
+        for i in range(len(pools)):
+            table[i].pool_k = self.pk[i].data_ptr()
+            table[i].pool_v = self.pv[i].data_ptr()
+            table[i].state_k = self.sk[i].data_ptr()
+            table[i].state_v = self.sv[i].data_ptr()
+        self.host_layers = table
+        raw = bytes(ctypes.string_at(ctypes.addressof(table), ctypes.sizeof(table)))
+        self.layers = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(self.device)
+
+    def set_pages(self, pages) -> None:
+        self.n_pages = len(pages)
+        self.pages = _dev(np.ascontiguousarray(pages, dtype=np.int32), self.device)
+
+    def args(self) -> binding.tf_state_args:
+        a = binding.tf_state_args()
+        a.n_layers = len(self.pk)
+        a.n_kv_heads = self.hkv
+        a.head_dim = self.head_dim
+        a.page_size = self.page_size
+        a.pool_pages = self.pool_pages
+        a.at = self.at
+        a.n_pages = self.n_pages
+        a.pages = self.pages.data_ptr()
+        a.layers = self.layers.data_ptr()
+        a.err = self.err.data_ptr()
+        return a
+
+    def save(self, stream: Optional[int] = None) -> None:
+        st = torch.cuda.current_stream(self.device).cuda_stream if stream is None else stream
+        check(binding.tf_state_save(self.args(), st), "tf_state_save")
+
+    def restore(self, stream: Optional[int] = None) -> None:
+        st = torch.cuda.current_stream(self.device).cuda_stream if stream is None else stream
+        check(binding.tf_state_restore(self.args(), st), "tf_state_restore")
+
+    def host(self):
+        """(pools, states) as lists of (K, V) host arrays."""
+        torch.cuda.synchronize(self.device)
+        pools = [(to_host_u16(k), to_host_u16(v)) for k, v in zip(self.pk, self.pv)]
+        states = [(to_host_u16(k), to_host_u16(v)) for k, v in zip(self.sk, self.sv)]
+        return pools, states
+
+    def error_word(self) -> int:
+        torch.cuda.synchronize(self.device)
+        return int(self.err.item())

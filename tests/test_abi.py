@@ -223,3 +223,38 @@ def test_put_refusals():
     assert binding.tf_kv_put(a, 0) == binding.TF_E_UNSUPPORTED
     a.page_size, a.k_new = 32, 0x10008
     assert binding.tf_kv_put(a, 0) == binding.TF_E_INVALID
+
+
+def _state_args(**kw):
+    a = binding.tf_state_args()
+    a.n_layers = kw.get("n_layers", 2)
+    a.n_kv_heads = kw.get("hkv", 8)
+    a.head_dim = kw.get("d", 64)
+    a.page_size = kw.get("page_size", 512)
+    a.pool_pages = kw.get("pool_pages", 100)
+    a.at = kw.get("at", 1000)
+    a.n_pages = kw.get("n_pages", 2)
+    a.pages = kw.get("pages", 0x10000)
+    a.layers = kw.get("layers", 0x20000)
+    a.err = None
+    return a
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(d=96), binding.TF_E_UNSUPPORTED),
+    (dict(page_size=48), binding.TF_E_UNSUPPORTED),
+    (dict(page_size=2048), binding.TF_E_UNSUPPORTED),
+    (dict(n_layers=-1), binding.TF_E_INVALID),
+    (dict(hkv=0), binding.TF_E_INVALID),
+    (dict(at=-1), binding.TF_E_INVALID),
+    (dict(pool_pages=0), binding.TF_E_INVALID),
+    (dict(at=1025, n_pages=2), binding.TF_E_PAST_PAGES),
+    (dict(pages=None), binding.TF_E_INVALID),
+    (dict(layers=None), binding.TF_E_INVALID),
+    (dict(at=0, pages=None, layers=None), binding.TF_OK),           # nothing to copy
+    (dict(n_layers=0, pages=None, layers=None), binding.TF_OK),
+])
+def test_state_copy_refusals(kw, rc):
+    # refused (or empty) before any launch: no GPU needed
+    assert binding.tf_state_save(_state_args(**kw), 0) == rc
+    assert binding.tf_state_restore(_state_args(**kw), 0) == rc

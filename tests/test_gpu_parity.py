@@ -199,13 +199,28 @@ def test_shapes_match_oracle(gpu, kind, d, hq, hkv, rows, keys, split):
     assert dw.error_word() == 0
 
 
-@pytest.mark.parametrize("page_size", [64, 256])
-def test_other_page_sizes(gpu, page_size):
-    w = synth.make_workload("pages", synth.KIND_PAGED, 8, 2, 128, [1, 3], [1000, 257], seed=8,
-                            page_size=page_size, pool_pages=40, split_keys=256)
+PAGE_SHAPES = [
+    # Hq, Hkv, D, rows, keys, split: decode (VALU) and prompt chunks (MFMA)
+    (8, 2, 128, [1, 3], [1000, 257], 256),
+    (8, 2, 128, [1, 1], [2100, 513], 512),
+    (8, 2, 64, [64], [1500], 512),          # D64 prompt chunk
+    (16, 2, 128, [128, 2], [3000, 700], 1024),   # D128 prompt chunk and a short verify
+    (16, 4, 256, [1, 24], [1200, 2500], 512),
+]
+
+
+@pytest.mark.parametrize("page_size", [64, 256, 512, 1024])
+@pytest.mark.parametrize("hq,hkv,d,rows,keys,split", PAGE_SHAPES)
+def test_other_page_sizes(gpu, page_size, hq, hkv, d, rows, keys, split):
+    print(f"P{page_size} D{d} {hq}/{hkv} rows {rows} keys {keys} split {split}", flush=True)
+    pool = sum(-(-k // page_size) for k in keys) + 3
+    w = synth.make_workload("pages", synth.KIND_PAGED, hq, hkv, d, rows, keys, seed=8 + d,
+                            page_size=page_size, pool_pages=pool, split_keys=split)
     dw = launch.DeviceWorkload(w, gpu)
+    assert dw.check_table() == binding.TF_OK
     dw.run()
     assert_close(dw.output(), oracle.attn_workload(w), rel=REL_SMALL, what=f"P{page_size}")
+    assert dw.error_word() == 0
 
 
 def test_different_split_sizes_agree_within_tolerance(gpu):
