@@ -25,7 +25,7 @@
  *    round's streams together": the rows kernel that reads each row's ring,
  *    slots and segment from a table and must equal one launch per segment;
  *    ring slots folded in groups with the next group in flight; the tree
- *    attention kernel beside it, whose trees equal their chains.
+ *    attention kernel beside it, checked to give the same drafts as chains.
  *  - TensorFold PR #1394, "lfm2: a cheaper DSpark hold": the drafter's block
  *    attention, the target's kernels with a FULL flag under which every row
  *    of a block sees the block's whole key range.
@@ -248,8 +248,9 @@ int tf_kv_put(const tf_put_args *a, hipStream_t stream);
 /*
  * Kept state copy (TensorFold PR #1503, the prompt-cache commit of the
  * lfm2_moe pool: a kept state holds every attention layer's keys and values
- * at positions [0, at), copied run by run with whole pages coalesced, and is
- * restored into the leased pages of the stream that resumes it).
+ * at positions [0, at), moved as runs of whole pages plus the last page's
+ * leading rows, and is restored into the pages of the stream that resumes
+ * it).
  *
  * tf_state_save copies positions [0, at) of every layer's K and V from the
  * stream's pool pages into the layer's state buffers; tf_state_restore copies
