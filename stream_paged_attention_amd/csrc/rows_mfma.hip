@@ -482,69 +482,26 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
         // -- values: O^T += V^T P^T per 16-dim block.  V^T fragment of lane
         // (lg, lc): dims 16 db + lc, keys 4 lg .. + 4 and 16 + 4 lg .. + 4,
         // by two transposed reads of 4 x 16 blocks
-        uint64_t bad = 0;
-        auto vfrag = [&](int db) {
-            i16x4_t h0, h1;
-            {
-                // the 16 lanes of group lg read the 4 x 16 block of keys
-                // 4 lg .. + 4 (resp. 16 + 4 lg ..), dims 16 db .. + 16: lane
-                // i of the group reads key 4 lg + i / 4, dims 16 db + 4 (i % 4) .. + 4
-                const int key0 = lg * 4 + (lc >> 2);
-                const int dim = db * 16 + (lc & 3) * 4;
-                const uint32_t o0 = unit_off<D>(key0, dim >> 3) + (dim & 7) * 2;
-                const uint32_t o1 = unit_off<D>(key0 + 16, dim >> 3) + (dim & 7) * 2;
-                h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4_t *)(vt_lds + o0));
-                h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4_t *)(vt_lds + o1));
-            }
-            u32x4_t vf = u32x4_t{(uint32_t)(uint16_t)h0[0] | ((uint32_t)(uint16_t)h0[1] << 16),
-                                 (uint32_t)(uint16_t)h0[2] | ((uint32_t)(uint16_t)h0[3] << 16),
-                                 (uint32_t)(uint16_t)h1[0] | ((uint32_t)(uint16_t)h1[1] << 16),
-                                 (uint32_t)(uint16_t)h1[2] | ((uint32_t)(uint16_t)h1[3] << 16)};
-            if (!full) {
-                // nonfinite values become 0 (exponent all ones -> zero); the
-                // indicator keeps which dims had one, per key slot
-                u32x4_t ind;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t x = vf[w];
-                    const bool nlo = (x & 0x7F80u) == 0x7F80u;
-                    const bool nhi = (x & 0x7F800000u) == 0x7F800000u;
-                    vf[w] = (nlo ? 0u : (x & 0xFFFFu)) | (nhi ? 0u : (x & 0xFFFF0000u));
-                    ind[w] = (nlo ? 0x3F80u : 0u) | (nhi ? 0x3F800000u : 0u);
-                    bad |= __builtin_amdgcn_ballot_w64(nlo || nhi);
-                }
-                if (bad != 0) {
-                    // count of visible nonfinite values per (dim, vector)
-#pragma unroll
-                    for (int b = 0; b < NQB; ++b) {
-                        u32x4_t visf;
-#pragma unroll
-                        for (int w = 0; w < 4; ++w) {
-                            const int ka = kt + (w >> 1) * 16 + lg * 4 + (w & 1) * 2;
-                            const bool v0 = row_sees<MASK>(ka, lim[b], tb, anc[b]);
-                            const bool v1 = row_sees<MASK>(ka + 1, lim[b], tb, anc[b]);
-                            visf[w] = (v0 ? 0x3F80u : 0u) | (v1 ? 0x3F800000u : 0u);
-                        }
-                        const f32x4_t cnt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            as_bf16x8(ind), as_bf16x8(visf), f32x4_t{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int bit = db * 4 + e;
-                            if (cnt[e] > 0.0f)
-                                nanmask[b][bit >> 5] |= 1u << (bit & 31);
-                        }
-                    }
-                }
-            }
-            return vf;
+        auto vread = [&](int db) {
+            // the 16 lanes of group lg read the 4 x 16 block of keys
+            // 4 lg .. + 4 (resp. 16 + 4 lg ..), dims 16 db .. + 16: lane
+            // i of the group reads key 4 lg + i / 4, dims 16 db + 4 (i % 4) .. + 4
+            const int key0 = lg * 4 + (lc >> 2);
+            const int dim = db * 16 + (lc & 3) * 4;
+            const uint32_t o0 = unit_off<D>(key0, dim >> 3) + (dim & 7) * 2;
+            const uint32_t o1 = unit_off<D>(key0 + 16, dim >> 3) + (dim & 7) * 2;
+            const i16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t *)(vt_lds + o0));
+            const i16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t *)(vt_lds + o1));
+            return u32x4_t{(uint32_t)(uint16_t)h0[0] | ((uint32_t)(uint16_t)h0[1] << 16),
+                           (uint32_t)(uint16_t)h0[2] | ((uint32_t)(uint16_t)h0[3] << 16),
+                           (uint32_t)(uint16_t)h1[0] | ((uint32_t)(uint16_t)h1[1] << 16),
+                           (uint32_t)(uint16_t)h1[2] | ((uint32_t)(uint16_t)h1[3] << 16)};
         };
-        // two dim blocks at a time: the rounded and the remainder products
-        // of one block are not back to back (independent chains)
-#pragma unroll
-        for (int db = 0; db < DB; db += 2) {
-            const u32x4_t v0 = vfrag(db), v1 = vfrag(db + 1);
+        // the products of two dim blocks: the rounded and the remainder
+        // terms of one block are not back to back (independent chains)
+        auto pv2 = [&](int db, const u32x4_t &v0, const u32x4_t &v1) {
 #pragma unroll
             for (int b = 0; b < NQB; ++b) {
                 o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v0), as_bf16x8(pf[b]), o[b][db], 0, 0, 0);
@@ -556,6 +513,78 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
                 o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v0), as_bf16x8(pl[b]), o[b][db], 0, 0, 0);
                 o[b][db + 1] =
                     __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v1), as_bf16x8(pl[b]), o[b][db + 1], 0, 0, 0);
+            }
+        };
+        // masked tile: nonfinite values become 0 (exponent all ones -> zero)
+        // and an indicator product records which (dim, vector) outputs saw
+        // one among their visible keys
+        uint64_t bad = 0;
+        auto vclean = [&](u32x4_t vf, int db) {
+            u32x4_t ind;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t x = vf[w];
+                const bool nlo = (x & 0x7F80u) == 0x7F80u;
+                const bool nhi = (x & 0x7F800000u) == 0x7F800000u;
+                vf[w] = (nlo ? 0u : (x & 0xFFFFu)) | (nhi ? 0u : (x & 0xFFFF0000u));
+                ind[w] = (nlo ? 0x3F80u : 0u) | (nhi ? 0x3F800000u : 0u);
+                bad |= __builtin_amdgcn_ballot_w64(nlo || nhi);
+            }
+            if (bad != 0) {
+                // count of visible nonfinite values per (dim, vector)
+#pragma unroll
+                for (int b = 0; b < NQB; ++b) {
+                    u32x4_t visf;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const int ka = kt + (w >> 1) * 16 + lg * 4 + (w & 1) * 2;
+                        const bool v0 = row_sees<MASK>(ka, lim[b], tb, anc[b]);
+                        const bool v1 = row_sees<MASK>(ka + 1, lim[b], tb, anc[b]);
+                        visf[w] = (v0 ? 0x3F80u : 0u) | (v1 ? 0x3F800000u : 0u);
+                    }
+                    const f32x4_t cnt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        as_bf16x8(ind), as_bf16x8(visf), f32x4_t{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int bit = db * 4 + e;
+                        if (cnt[e] > 0.0f)
+                            nanmask[b][bit >> 5] |= 1u << (bit & 31);
+                    }
+                }
+            }
+            return vf;
+        };
+        // The fragments of the next group of dim blocks are read while this
+        // group's products run (a double buffer of VG fragments; the
+        // scheduling barriers keep the compiler from reading further ahead
+        // than the registers allow), so no product waits on its own read.
+        constexpr int VG = D == 256 ? 2 : (DB < 4 ? DB : 4);
+        u32x4_t cur[VG], nxt[VG];
+#pragma unroll
+        for (int j = 0; j < VG; ++j)
+            cur[j] = vread(j);
+#pragma unroll
+        for (int g0 = 0; g0 < DB; g0 += VG) {
+            if (g0 + VG < DB) {
+#pragma unroll
+                for (int j = 0; j < VG; ++j)
+                    nxt[j] = vread(g0 + VG + j);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < VG; j += 2) {
+                u32x4_t v0 = cur[j], v1 = cur[j + 1];
+                if (!full) {
+                    v0 = vclean(v0, g0 + j);
+                    v1 = vclean(v1, g0 + j + 1);
+                }
+                pv2(g0 + j, v0, v1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (g0 + VG < DB) {
+#pragma unroll
+                for (int j = 0; j < VG; ++j)
+                    cur[j] = nxt[j];
             }
         }
     }
