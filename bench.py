@@ -44,7 +44,7 @@ def attn_flops(w) -> int:
     return total
 
 
-def traffic_entry(config: int):
+def traffic_entry(name: str):
     """HBM bytes per rows launch from the committed rocprofv3 counter runs, or None
     when the kernel source changed since they were taken."""
     try:
@@ -53,7 +53,7 @@ def traffic_entry(config: int):
     except (OSError, ValueError):
         return None
     from stream_paged_attention_amd.profsum import kernel_hash
-    e = data.get(f"config{config}")
+    e = data.get(name)
     if not e or e.get("kernel_hash") != kernel_hash():
         return None
     return e.get("hbm_bytes_per_launch")
@@ -63,7 +63,7 @@ def cpu_baseline(w, budget_s: float):
     from oracle import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
     rows = None
-    if w.name == "config4":        # bounded sample: a few rows of the prompt chunk
+    if w.name == "prompt512":      # bounded sample: a few rows of the prompt chunk
         rows = [0, 128, 256, 384, 511]
     reps, used = 0, threads
     t0 = time.perf_counter()
@@ -91,8 +91,8 @@ def bench_kv_put(args, w, dw, copies, stream) -> int:
     back to back; bytes = the rows' K and V read once and written once."""
     import numpy as np
     import torch
-    from stream_paged_attention_amd import binding
-    rng = np.random.Generator(np.random.PCG64(args.config + 100))
+    from stream_paged_attention_amd import binding, synth
+    rng = np.random.Generator(np.random.PCG64(synth.WORKLOAD_SEED[args.workload] + 100))
     shape = (w.total_rows, w.n_kv_heads, w.head_dim)
     k_new = torch.from_numpy(rng.integers(0, 1 << 16, size=shape, dtype=np.uint16).view(np.int16)).to(dw.device)
     v_new = torch.from_numpy(rng.integers(0, 1 << 16, size=shape, dtype=np.uint16).view(np.int16)).to(dw.device)
@@ -113,10 +113,10 @@ def bench_kv_put(args, w, dw, copies, stream) -> int:
     nbytes = 2 * 2 * w.total_rows * w.n_kv_heads * w.head_dim * 2
     gbps = nbytes / (ms * 1e-3) / 1e9
     print(json.dumps({
-        "metric": f"KV-append GB/s, synthetic workload {args.config}", "value": round(gbps, 2), "unit": "GB/s",
+        "metric": f"KV-append GB/s, synthetic workload {args.workload}", "value": round(gbps, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": synth_title(args.config) + " (round rows appended)", "rows": w.total_rows,
+        "config": {"workload": synth.WORKLOAD_TITLES[args.workload] + " (round rows appended)", "rows": w.total_rows,
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "bytes_per_step": nbytes,
                    "rows_per_s": round(w.total_rows / (ms * 1e-3), 1)},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 3), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -194,17 +194,14 @@ def bench_state(args) -> int:
     return 0
 
 
-def synth_title(n: int) -> str:
-    from stream_paged_attention_amd import synth
-    return synth.CONFIG_TITLES[n]
-
-
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--workload", default="decode16",
+                    choices=["single64", "decode16", "verify8", "prompt512", "ring17"],
+                    help="synthetic workload (decode16: the 16-stream decode the metric is quoted on)")
     ap.add_argument("--copies", type=int, default=0, help="K/V copies rotated (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -240,7 +237,7 @@ def main() -> int:
     binding.load()
     if args.op == "state":
         return bench_state(args)
-    w = synth.make_config(args.config)
+    w = synth.make_synthetic(args.workload)
     pool_bytes = (w.pool_k.nbytes * 2 if w.pool_k is not None
                   else sum(x.nbytes for x in w.store_k) * 2)
     copies = args.copies or max(1, min(8, -(-(2 * 256 * 2 ** 20) // max(1, kv_bytes(w)))))
@@ -302,17 +299,17 @@ def main() -> int:
     achieved_hbm = kvb / (rows_avg_ms * 1e-3) / 1e9
     # the prompt chunk is a dense contraction on the matrix cores; the decode,
     # verify and ring workloads read each key once and are bound by HBM
-    if args.config == 4:
+    if args.workload == "prompt512":
         bound, ach, peak, unit = "mfma", flops / (rows_avg_ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
         kernel = "tf_attn_rows (rows_mfma_kernel)"
     else:
         bound, ach, peak, unit = "hbm", achieved_hbm, HBM_PEAK_GBPS, "GB/s"
-        kernel = "tf_attn_rows (rows_valu_kernel)" if args.config in (1, 2) else \
+        kernel = "tf_attn_rows (rows_valu_kernel)" if args.workload in ("single64", "decode16") else \
             "tf_attn_rows (rows_mfma_kernel + rows_valu_kernel)"
-    traffic = traffic_entry(args.config)
+    traffic = traffic_entry(args.workload)
     out = {
-        "metric": METRIC if args.config == 2 else
-        f"KV-read GB/s and attn rows/s, synthetic workload {args.config}",
+        "metric": METRIC if args.workload == "decode16" else
+        f"KV-read GB/s and attn rows/s, synthetic workload {args.workload}",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -325,7 +322,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": synth.CONFIG_TITLES[args.config],
+            "workload": synth.WORKLOAD_TITLES[args.workload],
             "streams": len(w.segments), "rows": w.total_rows, "q_heads": w.n_q_heads,
             "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
             "split_keys": dw.split_keys, "kv_bytes_per_step": kvb, "attn_flops_per_step": flops,

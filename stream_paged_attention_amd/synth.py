@@ -339,44 +339,52 @@ def plant_tie(logits: np.ndarray, row: int, idx: Sequence[int]) -> None:
 # the five synthetic workloads
 # ----------------------------------------------------------------------------
 
-CONFIG_TITLES = {
-    1: "1 stream x 1 row, 8/2 heads, D64, 256 contiguous keys; argmax 1x1024 with a planted tie",
-    2: "16 one-row decode streams, 32/8 heads, D128, keys U[512,4096] in 32-token pages "
-       "of a permuted 4096-page pool, split-K 512 + merge",
-    3: "verify round: 8 streams of 1-16 causal rows, 16/4 heads, D256, committed keys "
-       "U[2048,16384] in 32-token pages; argmax over 128000 logits per row",
-    4: "prompt chunk: 1 stream, 512 causal rows over 15000 keys (14488 + 512), 16/4 heads, "
-       "D256, 32-token pages",
-    5: "ring drafter: 17 streams of 1-16 rows, 4200-slot rings with a random write head, "
-       "16/2 heads, D128; argmax 32x128000 with planted ties, a NaN row and a +Inf row",
+# Names, in the order their seeds were assigned: every value a workload holds
+# is drawn from numpy.random.Generator(PCG64(seed)) with this seed.
+WORKLOADS = ("single64", "decode16", "verify8", "prompt512", "ring17")
+WORKLOAD_SEED = {name: i + 1 for i, name in enumerate(WORKLOADS)}
+
+WORKLOAD_TITLES = {
+    "single64": "1 stream x 1 row, 8/2 heads, D64, 256 contiguous keys; argmax 1x1024 with a planted tie",
+    "decode16": "16 one-row decode streams, 32/8 heads, D128, keys U[512,4096] in 32-token pages "
+                "of a permuted 4096-page pool, split-K 512 + merge",
+    "verify8": "verify round: 8 streams of 1-16 causal rows, 16/4 heads, D256, committed keys "
+               "U[2048,16384] in 32-token pages; argmax over 128000 logits per row",
+    "prompt512": "prompt chunk: 1 stream, 512 causal rows over 15000 keys (14488 + 512), 16/4 heads, "
+                 "D256, 32-token pages",
+    "ring17": "ring drafter: 17 streams of 1-16 rows, 4200-slot rings with a random write head, "
+              "16/2 heads, D128; argmax 32x128000 with planted ties, a NaN row and a +Inf row",
 }
 
 # split_keys used for each workload (keys per partial; 0 = one partial per row-head)
-CONFIG_SPLIT = {1: 0, 2: 512, 3: 512, 4: 2048, 5: 512}
+WORKLOAD_SPLIT = {"single64": 0, "decode16": 512, "verify8": 512, "prompt512": 2048, "ring17": 512}
 
 
-def make_config(n: int) -> Workload:
-    """Build synthetic workload ``n`` (1..5) from seed ``n``."""
+def make_synthetic(name: str) -> Workload:
+    """Build the named synthetic workload (one of WORKLOADS) from its seed."""
+    if name not in WORKLOAD_SEED:
+        raise ValueError(f"no synthetic workload {name!r}")
+    n = WORKLOAD_SEED[name]
     rng = np.random.Generator(np.random.PCG64(n))
-    if n == 1:
-        w = make_workload("config1", KIND_CONTIG, 8, 2, 64, [1], [256], seed=n, rng=rng,
-                          split_keys=CONFIG_SPLIT[1])
+    if name == "single64":
+        w = make_workload("single64", KIND_CONTIG, 8, 2, 64, [1], [256], seed=n, rng=rng,
+                          split_keys=WORKLOAD_SPLIT["single64"])
         logits = normal_logits(rng, 1, 1024)
         idx = np.sort(rng.choice(1024, size=2, replace=False))
         plant_tie(logits, 0, idx)
         w.logits = logits
         w.notes = f"tie planted at ids {idx.tolist()}"
-    elif n == 2:
+    elif name == "decode16":
         kcs = rng.integers(512, 4096, size=16, endpoint=True)
-        w = make_workload("config2", KIND_PAGED, 32, 8, 128, [1] * 16, kcs.tolist(), seed=n,
-                          rng=rng, page_size=32, pool_pages=4096, split_keys=CONFIG_SPLIT[2])
-    elif n == 3:
+        w = make_workload("decode16", KIND_PAGED, 32, 8, 128, [1] * 16, kcs.tolist(), seed=n,
+                          rng=rng, page_size=32, pool_pages=4096, split_keys=WORKLOAD_SPLIT["decode16"])
+    elif name == "verify8":
         rows = rng.integers(1, 16, size=8, endpoint=True)
         committed = rng.integers(2048, 16384, size=8, endpoint=True)
         kcs = committed + rows
-        w = make_workload("config3", KIND_PAGED, 16, 4, 256, rows.tolist(), kcs.tolist(),
+        w = make_workload("verify8", KIND_PAGED, 16, 4, 256, rows.tolist(), kcs.tolist(),
                           seed=n, rng=rng, page_size=32, pool_pages=4608,
-                          split_keys=CONFIG_SPLIT[3])
+                          split_keys=WORKLOAD_SPLIT["verify8"])
         total = int(rows.sum())
         logits = normal_logits(rng, total, 128000)
         row = int(rng.integers(0, total))
@@ -384,15 +392,15 @@ def make_config(n: int) -> Workload:
         plant_tie(logits, row, idx)
         w.logits = logits
         w.notes = f"tie planted in row {row} at ids {idx.tolist()}"
-    elif n == 4:
-        w = make_workload("config4", KIND_PAGED, 16, 4, 256, [512], [15000], seed=n, rng=rng,
-                          page_size=32, pool_pages=1024, split_keys=CONFIG_SPLIT[4])
-    elif n == 5:
+    elif name == "prompt512":
+        w = make_workload("prompt512", KIND_PAGED, 16, 4, 256, [512], [15000], seed=n, rng=rng,
+                          page_size=32, pool_pages=1024, split_keys=WORKLOAD_SPLIT["prompt512"])
+    elif name == "ring17":
         heads = rng.integers(1, 4199, size=17, endpoint=True)
         rows = rng.integers(1, 16, size=17, endpoint=True)
-        w = make_workload("config5", KIND_RING, 16, 2, 128, rows.tolist(), [4200] * 17,
+        w = make_workload("ring17", KIND_RING, 16, 2, 128, rows.tolist(), [4200] * 17,
                           seed=n, rng=rng, ring_slots=[4200] * 17, ring_heads=heads.tolist(),
-                          split_keys=CONFIG_SPLIT[5])
+                          split_keys=WORKLOAD_SPLIT["ring17"])
         logits = normal_logits(rng, 32, 128000)
         plant_tie(logits, 0, [0, 127999])
         plant_tie(logits, 1, np.sort(rng.choice(128000, size=2, replace=False)))
@@ -403,9 +411,7 @@ def make_config(n: int) -> Workload:
         logits[5, int(rng.integers(0, 128000))] = BF16_POS_INF
         w.logits = logits
         w.notes = "ties in rows 0-3, NaN in row 4, +Inf in row 5"
-    else:
-        raise ValueError(f"no synthetic workload {n}")
-    w.name = f"config{n}"
+    w.name = name
     return w
 
 

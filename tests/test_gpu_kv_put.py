@@ -44,16 +44,16 @@ def test_put_then_attend_equals_preplaced(gpu, w):
     assert np.array_equal(a.output(), ref.output())
 
 
-def test_put_config_workloads(gpu):
-    # the round's rows of configs 2, 3 and 5 (decode, verify, ring drafter)
-    for n in (2, 3, 5):
-        w = synth.make_config(n)
+def test_put_synthetic_workloads(gpu):
+    # the round's rows of the decode, verify and ring drafter workloads
+    for name in ("decode16", "verify8", "ring17"):
+        w = synth.make_synthetic(name)
         before, k_new, v_new = round_inputs(w)
         dw = launch.DeviceWorkload(before, gpu)
         dw.kv_put(k_new, v_new)
         assert dw.error_word() == 0
         ek, ev = oracle_after(before, k_new, v_new)
-        assert _storage_equal(dw, ek, ev), f"config {n}"
+        assert _storage_equal(dw, ek, ev), name
 
 
 def test_put_error_bits_and_no_write(gpu):

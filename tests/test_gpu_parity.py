@@ -38,67 +38,67 @@ REL_SMALL = 2.0 ** -8
 
 
 @pytest.fixture(scope="module")
-def configs(gpu):
+def workloads(gpu):
     cache = {}
 
-    def get(n):
-        if n not in cache:
-            w = synth.make_config(n)
-            cache[n] = (w, launch.DeviceWorkload(w, gpu))
-        return cache[n]
+    def get(name):
+        if name not in cache:
+            w = synth.make_synthetic(name)
+            cache[name] = (w, launch.DeviceWorkload(w, gpu))
+        return cache[name]
     return get
 
 
 # --------------------------------------------------------------------------- the five workloads
 
-@pytest.mark.parametrize("n", [1, 2, 3, 5])
-def test_config_matches_oracle(configs, n):
-    w, dw = configs(n)
-    print(f"config {n}: {synth.CONFIG_TITLES[n]}", flush=True)
+@pytest.mark.parametrize("name", ["single64", "decode16", "verify8", "ring17"])
+def test_workload_matches_oracle(workloads, name):
+    w, dw = workloads(name)
+    print(f"{name}: {synth.WORKLOAD_TITLES[name]}", flush=True)
     assert dw.check_table() == binding.TF_OK
     dw.run()
     got = dw.output()
     ref = oracle.attn_workload(w)
-    err = assert_close(got, ref, what=f"config {n}")
+    err = assert_close(got, ref, what=name)
     assert dw.error_word() == 0
-    print(f"config {n}: max |err| = {err:.3e}")
+    print(f"{name}: max |err| = {err:.3e}")
 
 
-def test_config4_sampled_rows_match_oracle(configs):
-    w, dw = configs(4)
+def test_prompt512_sampled_rows_match_oracle(workloads):
+    w, dw = workloads("prompt512")
     dw.run()
     got = dw.output()
     rng = np.random.Generator(np.random.PCG64(44))
     rows = sorted(set([0, 1, 31, 32, 255, 256, 510, 511] + rng.choice(512, 16, replace=False).tolist()))
     ref = oracle.attn_workload(w, rows=rows)
-    err = assert_close(got[rows], ref, what="config 4 sampled rows")
+    err = assert_close(got[rows], ref, what="prompt512 sampled rows")
     assert dw.error_word() == 0
-    print(f"config 4: {len(rows)} sampled rows, max |err| = {err:.3e}")
+    print(f"prompt512: {len(rows)} sampled rows, max |err| = {err:.3e}")
 
 
-@pytest.mark.parametrize("n", [1, 3, 5])
-def test_config_argmax_bit_exact(configs, n):
-    w, _ = configs(n)
+@pytest.mark.parametrize("name", ["single64", "verify8", "ring17"])
+def test_workload_argmax_bit_exact(workloads, name):
+    w, _ = workloads(name)
     ids, flags = launch.argmax(w.logits)
     rids, rflags = oracle.argmax(w.logits)
     np.testing.assert_array_equal(ids, rids)
     np.testing.assert_array_equal(flags, rflags)
-    if n == 5:
+    if name == "ring17":
         assert flags[4] == 1 and flags[5] == 1 and flags[:4].sum() == 0
         assert ids[0] == 0
 
 
-@pytest.mark.parametrize("n", [2, 3, 5])
-def test_batched_equals_per_segment(configs, n):
-    w, dw = configs(n)
+@pytest.mark.parametrize("name", ["decode16", "verify8", "ring17"])
+def test_batched_equals_per_segment(workloads, name):
+    w, dw = workloads(name)
     dw.run()
     batched = dw.output()
     single = dw.run_per_segment()
-    assert np.array_equal(batched, single), f"config {n}: batched launch differs from per-segment"
+    assert np.array_equal(batched, single), f"{name}: batched launch differs from per-segment"
 
 
-def test_repeats_are_byte_identical(configs):
-    w, dw = configs(2)
+def test_repeats_are_byte_identical(workloads):
+    w, dw = workloads("decode16")
     outs = []
     for _ in range(5):
         dw.out.zero_()

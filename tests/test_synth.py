@@ -60,18 +60,18 @@ def test_contig_placement():
     assert (w.store_k[0][:, 9:, :] == synth.BF16_NAN).all()
 
 
-@pytest.mark.parametrize("n", [1, 2, 5])
-def test_config_structure(n):
-    w = synth.make_config(n)
-    if n == 1:
+@pytest.mark.parametrize("name", ["single64", "decode16", "ring17"])
+def test_workload_structure(name):
+    w = synth.make_synthetic(name)
+    if name == "single64":
         assert w.kind == synth.KIND_CONTIG and w.segments[0].key_count == 256
         assert w.logits.shape == (1, 1024)
-    if n == 2:
+    if name == "decode16":
         kcs = np.array([s.key_count for s in w.segments])
         assert len(kcs) == 16 and kcs.min() >= 512 and kcs.max() <= 4096
         assert w.pool_k.shape == (4096, 8, 32, 128)
         _check_paged(w)
-    if n == 5:
+    if name == "ring17":
         assert len(w.segments) == 17 and all(s.capacity == 4200 == s.key_count for s in w.segments)
         assert w.logits.shape == (32, 128000)
         assert w.total_rows == sum(s.n_rows for s in w.segments)
@@ -79,7 +79,7 @@ def test_config_structure(n):
             np.testing.assert_array_equal(synth.gather_ring(w.store_k[i], s.first, s.key_count), w.k_logical[i])
 
 
-def test_configs_are_deterministic():
-    a, b = synth.make_config(1), synth.make_config(1)
+def test_workloads_are_deterministic():
+    a, b = synth.make_synthetic("single64"), synth.make_synthetic("single64")
     np.testing.assert_array_equal(a.q, b.q)
     np.testing.assert_array_equal(a.logits, b.logits)
