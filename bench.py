@@ -214,8 +214,8 @@ def main() -> int:
                     help="only run 20 plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by stream or kv head with no exchange; see DESIGN.md)",
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by stream or by kv head with no exchange between GPUs)",
               file=sys.stderr)
         return 2
 

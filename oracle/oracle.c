@@ -33,7 +33,7 @@
  *    commit and its contract entry: ties go to the lower id).  A NaN ranks
  *    as -inf when choosing the id (PR #1503, the router note in lfm2_moe.cu).
  *
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings where the pages are silent:
  *  - GQA: query head h reads kv head h / (Hq / Hkv) (contiguous groups).
  *  - NaN rule: if any *visible* score of a (row, head) is NaN or +-Inf, all
  *    of that (row, head)'s outputs are NaN; otherwise an output element whose

@@ -1,6 +1,6 @@
 """GPU parity of the HIP path against the float64 oracle, and its equalities.
 
-Tolerance (spec contract): |bf16 output - float64 oracle| <= 2e-3 for the
+Tolerance: |bf16 output - float64 oracle| <= 2e-3 for the
 five synthetic workloads, NaN positions identical; argmax ids and flags
 bit-exact.  Small hand-shaped cases can produce outputs of magnitude >= 0.5,
 where bf16's own half-ulp (2^-9 |x|) exceeds 2e-3; there the bound is
