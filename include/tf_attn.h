@@ -12,18 +12,20 @@
  *
  * Sources (the pages this library is built from):
  *  - TensorFold PR #1503, "lfm2_moe CUDA: attention pages from the shared KV
- *    pool, and the prompt cache": the segment table of cache addresses, row
- *    offsets and key counts that lets one launch per layer serve every stream
+ *    pool, and the prompt cache": a per-stream table (where the stream's
+ *    cache is, which packed rows are its own, how many keys it holds) that
+ *    lets one launch per layer serve every stream
  *    (the shared-rounds commit); reads through a slot's page table and the
  *    refusal of rows past a slot's pages (the pool-leasing commit); the GPU
  *    argmax with its tie and nonfinite rules (the lfm2_argmax commit).
  *  - TensorFold PR #1653, "spark25 CUDA: the full layers' caches in pages of
  *    the core pool ...": paged decode part/merge kernels, prompt rows read
- *    through the slot's page-table row in pages of whole 32-key tiles, the
- *    page lookup hoisted out of the key loop.
+ *    through the slot's page-table row in pages of whole 32-key tiles, with
+ *    the page id looked up once per chunk instead of once per key.
  *  - TensorFold PR #1562, "Qwen3.6 MTP drafter on CUDA: draft a shared
- *    round's streams together": the rows kernel that reads each row's ring,
- *    slots and segment from a table and must equal one launch per segment;
+ *    round's streams together": one rows kernel for all streams, each packed
+ *    row finding its ring and slot count through a table, bit-equal to a
+ *    launch per stream;
  *    ring slots folded in groups with the next group in flight; the tree
  *    attention kernel beside it, checked to give the same drafts as chains.
  *  - TensorFold PR #1394, "lfm2: a cheaper DSpark hold": the drafter's block
@@ -247,8 +249,8 @@ int tf_kv_put(const tf_put_args *a, hipStream_t stream);
 
 /*
  * Kept state copy (TensorFold PR #1503, the prompt-cache commit of the
- * lfm2_moe pool: a kept state holds every attention layer's keys and values
- * at positions [0, at), moved as runs of whole pages plus the last page's
+ * lfm2_moe pool: a kept state holds the K and V rows of positions [0, at)
+ * for every attention layer, moved as runs of whole pages plus the last page's
  * leading rows, and is restored into the pages of the stream that resumes
  * it).
  *

@@ -1,6 +1,6 @@
-"""Reference kept-state copy: a stream's keys and values at positions [0, at).
+"""Reference kept-state copy: the K and V rows of a stream's positions [0, at).
 
-TEST INFRASTRUCTURE ONLY: imported by tests/ and the bench's CPU-baseline leg;
+TEST INFRASTRUCTURE ONLY: imported by tests/ (and nothing else);
 the HIP library never imports it and shares no code with it.
 
 What it computes (TensorFold PR #1503, the prompt-cache commit of the

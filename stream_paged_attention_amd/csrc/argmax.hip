@@ -1,7 +1,7 @@
 // tf_argmax: greedy pick of each row's first largest logit, with a flag on
 // rows that hold a NaN or +-Inf (TensorFold PR #1503, the lfm2_argmax commit:
-// ties to the lower id, nonfinite rows flagged; the router note: NaN ranks as
-// -inf).
+// equal maxima resolve to the smaller id and a nonfinite row is flagged; the
+// router note: a NaN counts as -inf).
 //
 // Every logit becomes an order-preserving key: its bf16 value mapped to an
 // unsigned 16-bit rank (NaN taken as -inf, -0.0 as +0.0) above the complement

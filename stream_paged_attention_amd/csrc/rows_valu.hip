@@ -4,8 +4,8 @@
 // Work item = one workgroup = (segment, kv head g, split t).  It serves every
 // query vector of the segment that reads kv head g: its n_rows rows times
 // the group's Hq/Hkv query heads (TensorFold PR #1503: one launch serves all
-// streams' rows from the segment table; PR #1562: each row's ring, slots and
-// segment come from the table).
+// streams' rows from the segment table; PR #1562: a packed row finds its
+// ring and slot count through the table).
 //
 // Inside a work item the split's keys are cut into tiles of TK keys (a tile
 // never crosses a page: pages hold whole tiles, PR #1653).  Wave w takes
@@ -15,8 +15,8 @@
 // 128-byte lines of consecutive keys.  The next tile's loads are issued
 // before the current tile is folded (the ring's slot groups in flight one
 // ahead, PR #1562).  The page id of every tile a wave will read is fetched
-// once, one lane per tile, and taken out with readlane (the per-chunk page
-// lookup hoisted out of the key loop, PR #1653).
+// once, one lane per tile, and taken out with readlane (PR #1653 likewise
+// looks a page id up once per chunk, not once per key).
 //
 // Scores: v_dot2_f32_bf16 on packed bf16 pairs, then a DPP sum over the key
 // group.  Online softmax per query vector with a wave-wide reference m (raw

@@ -1,4 +1,4 @@
-// tf_state_save / tf_state_restore: copy a stream's keys and values at
+// tf_state_save / tf_state_restore: copy the K and V rows of a stream's
 // positions [0, at) between its pool pages and a kept state (TensorFold
 // PR #1503, the prompt-cache commit: whole pages copied as units, then the
 // last page's rows; the state restored into the resuming stream's pages).
