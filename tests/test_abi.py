@@ -35,10 +35,20 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name)
 
 
-def test_header_compiles_as_c_and_struct_sizes_match():
+STRUCTS = ("tf_segment", "tf_attn_args", "tf_put_args", "tf_state_layer", "tf_state_args")
+
+
+def test_header_compiles_as_c_and_struct_layouts_match():
+    # every field's offset and every struct's size, as a C compiler lays
+    # them out, against the ctypes declarations of the binding
+    lines = []
+    for name in STRUCTS:
+        cls = getattr(binding, name)
+        lines.append(f'printf("{name} size %zu\\n", sizeof({name}));')
+        for field, _ in cls._fields_:
+            lines.append(f'printf("{name} {field} %zu\\n", offsetof({name}, {field}));')
     src = ("#include \"tf_attn.h\"\n#include <stdio.h>\n#include <stddef.h>\n"
-           "int main(void){printf(\"%zu %zu %zu\\n\", sizeof(tf_segment), sizeof(tf_attn_args),"
-           " offsetof(tf_attn_args, segs)); return 0;}\n")
+           "int main(void){" + "".join(lines) + " return 0;}\n")
     tmp = os.path.join(ROOT, "_build")
     os.makedirs(tmp, exist_ok=True)
     c = os.path.join(tmp, "hdr_check.c")
@@ -47,9 +57,15 @@ def test_header_compiles_as_c_and_struct_sizes_match():
     subprocess.check_call(["gcc", "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
                            "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
                            c, "-o", exe])
-    sizes = [int(x) for x in subprocess.check_output([exe]).split()]
-    assert sizes == [ctypes.sizeof(binding.tf_segment), ctypes.sizeof(binding.tf_attn_args),
-                     binding.tf_attn_args.segs.offset]
+    got = {}
+    for line in subprocess.check_output([exe], text=True).splitlines():
+        name, what, val = line.split()
+        got[(name, what)] = int(val)
+    for name in STRUCTS:
+        cls = getattr(binding, name)
+        assert got[(name, "size")] == ctypes.sizeof(cls), name
+        for field, _ in cls._fields_:
+            assert got[(name, field)] == getattr(cls, field).offset, (name, field)
 
 
 def test_strerror_names_every_code():
