@@ -33,6 +33,25 @@ __device__ __forceinline__ float merge_wave_sum(float x)
     return x;
 }
 
+// Load the lane's DL floats of o from a record (16-, 8- or 4-byte aligned).
+template <int DL>
+__device__ __forceinline__ void load_o(const float *src, float (&dst)[DL])
+{
+    if constexpr (DL == 4) {
+        const float4 x = *reinterpret_cast<const float4 *>(src);
+        dst[0] = x.x;
+        dst[1] = x.y;
+        dst[2] = x.z;
+        dst[3] = x.w;
+    } else if constexpr (DL == 2) {
+        const float2 x = *reinterpret_cast<const float2 *>(src);
+        dst[0] = x.x;
+        dst[1] = x.y;
+    } else {
+        dst[0] = src[0];
+    }
+}
+
 // Merge the n_splits records starting at `rec` (record stride D + 4 floats)
 // into dst[0 .. D) (bf16).  parts_ok false: write NaN.
 template <int D>
@@ -46,12 +65,13 @@ __device__ __forceinline__ void merge_one(const float *rec, int n_splits, bool p
         acc[i] = 0.0f;
     bool nan_out = !parts_ok;
     if (parts_ok) {
-        float big = -INFINITY;
-        bool bad = false;
-        for (int t = lane; t < n_splits; t += 64) {
-            const float mt = rec[(int64_t)t * RS];
-            bad = bad || __builtin_isnan(mt);
-            big = fmaxf(big, mt);
+        // lane t holds split t's (m, l), read together; splits past 64 are
+        // read in a loop
+        float ml = -INFINITY, ll = 0.0f;
+        if (lane < n_splits) {
+            const float2 x = *reinterpret_cast<const float2 *>(rec + (int64_t)lane * RS);
+            ml = x.x;
+            ll = x.y;
         }
         // the first chunk of o is in flight while the maxima reduce
         float of[kMergeChunk][DL];
@@ -59,33 +79,32 @@ __device__ __forceinline__ void merge_one(const float *rec, int n_splits, bool p
 #pragma unroll
         for (int u = 0; u < kMergeChunk; ++u)
             if (u < c0)
-#pragma unroll
-                for (int i = 0; i < DL; ++i)
-                    of[u][i] = rec[(int64_t)u * RS + 4 + lane * DL + i];
+                load_o<DL>(rec + (int64_t)u * RS + 4 + lane * DL, of[u]);
+        bool bad = __builtin_isnan(ml);
+        float big = ml;
+        for (int t = lane + 64; t < n_splits; t += 64) {
+            const float mt = rec[(int64_t)t * RS];
+            bad = bad || __builtin_isnan(mt);
+            big = fmaxf(big, mt);
+        }
         big = merge_wave_max(big);
         nan_out = __builtin_amdgcn_ballot_w64(bad) != 0 || big == -INFINITY;
-        float lsum = 0.0f;
-        for (int t = lane; t < n_splits; t += 64) {
+        // weight of split t, computed by lane t (splits past 64 directly)
+        const float wl = (ml == -INFINITY) ? 0.0f : exp2_fast((ml - big) * kLog2e);
+        float lsum = ll * wl;
+        for (int t = lane + 64; t < n_splits; t += 64) {
             const float mt = rec[(int64_t)t * RS];
             if (mt != -INFINITY)
                 lsum += rec[(int64_t)t * RS + 1] * exp2_fast((mt - big) * kLog2e);
         }
         lsum = merge_wave_sum(lsum);
-        // weight of split t, computed by lane t (splits past 64 directly)
-        float wl = 0.0f;
-        if (lane < n_splits) {
-            const float mt = rec[(int64_t)lane * RS];
-            wl = (mt == -INFINITY) ? 0.0f : exp2_fast((mt - big) * kLog2e);
-        }
         for (int t0 = 0; t0 < n_splits; t0 += kMergeChunk) {
             const int cn = min(n_splits - t0, kMergeChunk);
             if (t0 > 0) {
 #pragma unroll
                 for (int u = 0; u < kMergeChunk; ++u)
                     if (u < cn)
-#pragma unroll
-                        for (int i = 0; i < DL; ++i)
-                            of[u][i] = rec[(int64_t)(t0 + u) * RS + 4 + lane * DL + i];
+                        load_o<DL>(rec + (int64_t)(t0 + u) * RS + 4 + lane * DL, of[u]);
             }
 #pragma unroll
             for (int u = 0; u < kMergeChunk; ++u) {
