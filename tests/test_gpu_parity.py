@@ -177,6 +177,10 @@ SHAPES = [
     ("paged", 128, 16, 4, [6], [5000], 0),         # one split of 157 tiles: page ids reloaded
     ("contig", 64, 8, 2, [20], [333], 0),
     ("ring", 256, 16, 4, [5, 16], [4100, 700], 1024),
+    # more than 64 splits a row: the merge reads the splits past 64 in a loop
+    ("paged", 128, 32, 8, [1, 1], [131072, 3000], 512),   # a long decode context, 256 splits
+    ("paged", 128, 8, 2, [1, 3], [20000, 20000], 32),    # 625 splits, both rows kernels
+    ("contig", 64, 64, 1, [1], [2100], 32),              # 64 query heads on one kv head (MFMA)
 ]
 
 
