@@ -229,6 +229,10 @@ int tf_attn_rows(const tf_attn_args *a, hipStream_t stream)
     // short verify) run on the VALU kernel, the others on the MFMA kernel;
     // the choice depends on the segment alone.
     const int64_t nq_max = (int64_t)a->max_rows * p.group;
+    const int64_t n_qt = (nq_max + tfa::mfma_query_tile(a->head_dim) - 1) / tfa::mfma_query_tile(a->head_dim);
+    if (nq_max > p.mfma_min_q &&
+        n_qt * p.n_split_max * p.n_segments * p.hkv > (int64_t)INT32_MAX / 512)
+        return TF_E_UNSUPPORTED;
     if (a->min_rows > 0 && (int64_t)a->min_rows * p.group > p.mfma_min_q) {
         // every segment has many query vectors: no decode launch, and the
         // matrix-core kernel takes all segments (so none is dropped even if
@@ -238,9 +242,6 @@ int tf_attn_rows(const tf_attn_args *a, hipStream_t stream)
         return TF_E_LAUNCH;
     }
     if (nq_max > p.mfma_min_q) {
-        const int n_qt = (int)((nq_max + tfa::mfma_query_tile(a->head_dim) - 1) / tfa::mfma_query_tile(a->head_dim));
-        if ((int64_t)n_qt * p.n_split_max * p.n_segments * p.hkv > (int64_t)INT32_MAX / 512)
-            return TF_E_UNSUPPORTED;
         if (tfa::launch_rows_mfma(p, a->head_dim, a->kind, (int)nq_max, stream) != hipSuccess)
             return TF_E_LAUNCH;
     }
