@@ -66,6 +66,11 @@ struct MGeo {
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == TILE, "tile must split into 1 KB wave loads");
 };
 
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
@@ -245,8 +250,23 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
     const float c = p.c_log2;
     const float lazy = kMLazy / c;
 
-    // ---- this lane's query vectors (one per 16-vector block) and limits
-    const int qv0 = qt * QB + wave * (16 * NQB);
+    // ---- which query vectors and output dims this wave computes.  A tile
+    // with fewer 16-vector blocks than waves gives each block kw waves (a
+    // power of two): they compute the same scores and weights, and each
+    // accumulates 1 / kw of the output dims.  Every (vector, dim) output goes
+    // through the same operations whatever kw is; the other waves of the
+    // workgroup only stop idling.  kw is uniform over the workgroup and
+    // selects one of the compiled loop bodies below.
+    static_assert(NQB == 1, "the dim split assumes one 16-vector block per wave");
+    constexpr int KW_MAX = NW < DB / 2 ? NW : DB / 2;
+    const int nvb = min(NW, (nq - qt * QB + 15) / 16);   // blocks holding a vector
+    int kw = KW_MAX;
+    while (kw > 1 && NW / kw < nvb)
+        kw >>= 1;
+    const int nb = NW / kw;       // blocks served at once
+    const int dg = wave / nb;     // dim group, 0 .. kw - 1
+    // block wave % nb; a block at or past nvb holds no vector (the wave idles)
+    const int qv0 = qt * QB + (wave % nb) * 16;
     int lim[NQB];
     uint64_t anc[NQB];
     int tb = INT32_MAX;   // the segment's first new key under a tree mask
@@ -358,330 +378,345 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
         }
     };
 
-    // ---- state per block of 16 query vectors (per lane: its vector)
-    float m[NQB], mc[NQB], thr[NQB], lo[NQB];
-    f32x4_t o[NQB][DB];
-    f32x4_t lsum[NQB];   // ones-block product: every element is l of the lane's vector
-    uint32_t nanmask[NQB][(DB * 4 + 31) / 32];
-#pragma unroll
-    for (int b = 0; b < NQB; ++b) {
-        m[b] = -INFINITY;
-        mc[b] = 0.0f;
-        thr[b] = -INFINITY;
-        lo[b] = INFINITY;
-        lsum[b] = f32x4_t{0, 0, 0, 0};
-#pragma unroll
-        for (int d = 0; d < DB; ++d)
-            o[b][d] = f32x4_t{0, 0, 0, 0};
-#pragma unroll
-        for (int w = 0; w < (DB * 4 + 31) / 32; ++w)
-            nanmask[b][w] = 0;
-    }
-    const uint32_t one2 = 0x3F803F80u;   // two bf16 ones
-    const bf16x8_t ones = as_bf16x8(u32x4_t{one2, one2, one2, one2});
-
-    // Q fragments and the first page ids complete before the pipeline
-    // starts: a register load still pending inside the loop would make every
-    // iteration wait for all loads (the tile loads issued from asm included)
-    if (n_tiles > 0)
-        load_pids(0);
-    wait_vm<0>();
-#pragma unroll
-    for (int u = 0; u < PD; ++u)
-        if (u < n_tiles)
-            issue(u, u);
-    for (int i = 0; i < n_tiles; ++i) {
-        const int buf = i % NBUF;
-        const int kt = k0 + i * kKT;
-        // tiles i .. i + PD - 1 are in flight (those that exist); wait for
-        // the oldest.  The LDS reads of tile i - 1 are complete (their
-        // products consumed them) before this wave reaches the barrier.
-        const int newer = min(PD - 1, n_tiles - 1 - i);
-        wait_tiles<2 * LOADS, PD - 1>(newer);
-        // after the barrier: every wave's loads of tile i have landed and
-        // every wave is done with tile i - 1, whose buffer takes tile i + PD
-        tile_barrier();
-        if (i + PD < n_tiles) {
-            if (((i + PD) & 63) == 0) {
-                // next batch of page ids (every 64 tiles): drains the tiles in flight
-                load_pids(i + PD);
-                wait_vm<0>();
-            }
-            issue(i + PD, (i + PD) % NBUF);
+    // ---- the tile loop and the write, for kw = KW waves a block
+    auto body = [&](auto kw_c) {
+        constexpr int KW = decltype(kw_c)::value;
+        constexpr int DBG = DB / KW;   // dim blocks of this wave
+        const int db0 = dg * DBG;
+        // ---- state per block of 16 query vectors (per lane: its vector)
+        float m[NQB], mc[NQB], thr[NQB], lo[NQB];
+        f32x4_t o[NQB][DBG];   // o[b][j]: dim block db0 + j
+        f32x4_t lsum[NQB];   // ones-block product: every element is l of the lane's vector
+        uint32_t nanmask[NQB][(DBG * 4 + 31) / 32];
+    #pragma unroll
+        for (int b = 0; b < NQB; ++b) {
+            m[b] = -INFINITY;
+            mc[b] = 0.0f;
+            thr[b] = -INFINITY;
+            lo[b] = INFINITY;
+            lsum[b] = f32x4_t{0, 0, 0, 0};
+    #pragma unroll
+            for (int d = 0; d < DBG; ++d)
+                o[b][d] = f32x4_t{0, 0, 0, 0};
+    #pragma unroll
+            for (int w = 0; w < (DBG * 4 + 31) / 32; ++w)
+                nanmask[b][w] = 0;
         }
-        if (!wave_live || kt >= lim_max)
-            continue;    // nothing visible to this wave in the tile
-        const char *kt_lds = kv_lds[buf][0];
-        const char *vt_lds = kv_lds[buf][1];
-        const bool full = kt + kKT <= lim_min;
+        const uint32_t one2 = 0x3F803F80u;   // two bf16 ones
+        const bf16x8_t ones = as_bf16x8(u32x4_t{one2, one2, one2, one2});
 
-        // -- scores S^T: 2 key blocks x NQB vector blocks
-        // (even and odd dim steps accumulate apart: four independent
-        // product chains per vector block keep the matrix pipe busy)
-        f32x4_t s[NQB][2], s2[NQB][2];
-#pragma unroll
-        for (int b = 0; b < NQB; ++b)
-            s[b][0] = s[b][1] = s2[b][0] = s2[b][1] = f32x4_t{0, 0, 0, 0};
-#pragma unroll
-        for (int ks = 0; ks < KS; ks += 2) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-#pragma unroll
+        // Q fragments and the first page ids complete before the pipeline
+        // starts: a register load still pending inside the loop would make every
+        // iteration wait for all loads (the tile loads issued from asm included)
+        if (n_tiles > 0)
+            load_pids(0);
+        wait_vm<0>();
+    #pragma unroll
+        for (int u = 0; u < PD; ++u)
+            if (u < n_tiles)
+                issue(u, u);
+        for (int i = 0; i < n_tiles; ++i) {
+            const int buf = i % NBUF;
+            const int kt = k0 + i * kKT;
+            // tiles i .. i + PD - 1 are in flight (those that exist); wait for
+            // the oldest.  The LDS reads of tile i - 1 are complete (their
+            // products consumed them) before this wave reaches the barrier.
+            const int newer = min(PD - 1, n_tiles - 1 - i);
+            wait_tiles<2 * LOADS, PD - 1>(newer);
+            // after the barrier: every wave's loads of tile i have landed and
+            // every wave is done with tile i - 1, whose buffer takes tile i + PD
+            tile_barrier();
+            if (i + PD < n_tiles) {
+                if (((i + PD) & 63) == 0) {
+                    // next batch of page ids (every 64 tiles): drains the tiles in flight
+                    load_pids(i + PD);
+                    wait_vm<0>();
+                }
+                issue(i + PD, (i + PD) % NBUF);
+            }
+            if (!wave_live || kt >= lim_max)
+                continue;    // nothing visible to this wave in the tile
+            const char *kt_lds = kv_lds[buf][0];
+            const char *vt_lds = kv_lds[buf][1];
+            const bool full = kt + kKT <= lim_min;
+
+            // -- scores S^T: 2 key blocks x NQB vector blocks
+            // (even and odd dim steps accumulate apart: four independent
+            // product chains per vector block keep the matrix pipe busy)
+            f32x4_t s[NQB][2], s2[NQB][2];
+    #pragma unroll
+            for (int b = 0; b < NQB; ++b)
+                s[b][0] = s[b][1] = s2[b][0] = s2[b][1] = f32x4_t{0, 0, 0, 0};
+    #pragma unroll
+            for (int ks = 0; ks < KS; ks += 2) {
+    #pragma unroll
+                for (int h = 0; h < 2; ++h) {
+    #pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(
+                            kt_lds + unit_off<D>(kb * 16 + lc, (ks + h) * 4 + lg));
+    #pragma unroll
+                        for (int b = 0; b < NQB; ++b) {
+                            f32x4_t &acc = h ? s2[b][kb] : s[b][kb];
+                            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[b][ks + h]),
+                                                                         acc, 0, 0, 0);
+                        }
+                    }
+                }
+            }
+    #pragma unroll
+            for (int b = 0; b < NQB; ++b) {
+                s[b][0] += s2[b][0];
+                s[b][1] += s2[b][1];
+            }
+
+            // -- online softmax per vector; P^T fragments in bf16
+            u32x4_t pf[NQB], pl[NQB];   // P^T in bf16: rounded value and its remainder
+            uint64_t need = 0;
+            float tmax[NQB];
+    #pragma unroll
+            for (int b = 0; b < NQB; ++b) {
+                float mx = -INFINITY;
+    #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(
-                        kt_lds + unit_off<D>(kb * 16 + lc, (ks + h) * 4 + lg));
-#pragma unroll
-                    for (int b = 0; b < NQB; ++b) {
-                        f32x4_t &acc = h ? s2[b][kb] : s[b][kb];
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[b][ks + h]),
-                                                                     acc, 0, 0, 0);
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float x = s[b][kb][e];
+                        if (!full) {
+                            const int key = kt + kb * 16 + lg * 4 + e;
+                            const bool vis = row_sees<MASK>(key, lim[b], tb, anc[b]);
+                            lo[b] = min2(lo[b], vis ? x : INFINITY);
+                            x = vis ? x : -INFINITY;
+                            s[b][kb][e] = x;
+                        } else {
+                            lo[b] = min2(lo[b], x);
+                        }
+                        mx = max2(mx, x);
                     }
                 }
+                float a, bb;
+                swap16(mx, a, bb);
+                mx = max2(a, bb);
+                swap32(mx, a, bb);
+                mx = max2(a, bb);
+                tmax[b] = mx;
+                need |= __builtin_amdgcn_ballot_w64(mx > thr[b]);
             }
-        }
-#pragma unroll
-        for (int b = 0; b < NQB; ++b) {
-            s[b][0] += s2[b][0];
-            s[b][1] += s2[b][1];
-        }
-
-        // -- online softmax per vector; P^T fragments in bf16
-        u32x4_t pf[NQB], pl[NQB];   // P^T in bf16: rounded value and its remainder
-        uint64_t need = 0;
-        float tmax[NQB];
-#pragma unroll
-        for (int b = 0; b < NQB; ++b) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float x = s[b][kb][e];
-                    if (!full) {
-                        const int key = kt + kb * 16 + lg * 4 + e;
-                        const bool vis = row_sees<MASK>(key, lim[b], tb, anc[b]);
-                        lo[b] = min2(lo[b], vis ? x : INFINITY);
-                        x = vis ? x : -INFINITY;
-                        s[b][kb][e] = x;
-                    } else {
-                        lo[b] = min2(lo[b], x);
-                    }
-                    mx = max2(mx, x);
-                }
-            }
-            float a, bb;
-            swap16(mx, a, bb);
-            mx = max2(a, bb);
-            swap32(mx, a, bb);
-            mx = max2(a, bb);
-            tmax[b] = mx;
-            need |= __builtin_amdgcn_ballot_w64(mx > thr[b]);
-        }
-        if (need != 0) {
-#pragma unroll
-            for (int b = 0; b < NQB; ++b) {
-                const bool up = tmax[b] > m[b];
-                const float alpha = up ? exp2_fast((m[b] - tmax[b]) * c) : 1.0f;
-                m[b] = up ? tmax[b] : m[b];
-                mc[b] = up ? tmax[b] * c : mc[b];
-                thr[b] = up ? tmax[b] + lazy : thr[b];
-                lsum[b] *= alpha;
-#pragma unroll
-                for (int d = 0; d < DB; ++d)
-                    o[b][d] *= alpha;
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < NQB; ++b) {
-            float pe[8];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    pe[kb * 4 + e] = exp2_fast(fmaf(s[b][kb][e], c, -mc[b]));
-            // p = hi + lo, both bf16: the value product takes the two parts, so
-            // the weights keep about 16 significant bits instead of 8
-            float pr[8];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                pf[b][w] = pack_bf16(pe[2 * w], pe[2 * w + 1]);
-                pr[2 * w] = pe[2 * w] - bf16_lo(pf[b][w]);
-                pr[2 * w + 1] = pe[2 * w + 1] - bf16_hi(pf[b][w]);
-            }
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-                pl[b][w] = pack_bf16(pr[2 * w], pr[2 * w + 1]);
-            lsum[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, as_bf16x8(pf[b]), lsum[b], 0, 0, 0);
-            lsum[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, as_bf16x8(pl[b]), lsum[b], 0, 0, 0);
-        }
-
-        // -- values: O^T += V^T P^T per 16-dim block.  V^T fragment of lane
-        // (lg, lc): dims 16 db + lc, keys 4 lg .. + 4 and 16 + 4 lg .. + 4,
-        // by two transposed reads of 4 x 16 blocks
-        auto vread = [&](int db) {
-            // the 16 lanes of group lg read the 4 x 16 block of keys
-            // 4 lg .. + 4 (resp. 16 + 4 lg ..), dims 16 db .. + 16: lane
-            // i of the group reads key 4 lg + i / 4, dims 16 db + 4 (i % 4) .. + 4
-            const int key0 = lg * 4 + (lc >> 2);
-            const int dim = db * 16 + (lc & 3) * 4;
-            const uint32_t o0 = unit_off<D>(key0, dim >> 3) + (dim & 7) * 2;
-            const uint32_t o1 = unit_off<D>(key0 + 16, dim >> 3) + (dim & 7) * 2;
-            const i16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4_t *)(vt_lds + o0));
-            const i16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4_t *)(vt_lds + o1));
-            return u32x4_t{(uint32_t)(uint16_t)h0[0] | ((uint32_t)(uint16_t)h0[1] << 16),
-                           (uint32_t)(uint16_t)h0[2] | ((uint32_t)(uint16_t)h0[3] << 16),
-                           (uint32_t)(uint16_t)h1[0] | ((uint32_t)(uint16_t)h1[1] << 16),
-                           (uint32_t)(uint16_t)h1[2] | ((uint32_t)(uint16_t)h1[3] << 16)};
-        };
-        // the products of two dim blocks: the rounded and the remainder
-        // terms of one block are not back to back (independent chains)
-        auto pv2 = [&](int db, const u32x4_t &v0, const u32x4_t &v1) {
-#pragma unroll
-            for (int b = 0; b < NQB; ++b) {
-                o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v0), as_bf16x8(pf[b]), o[b][db], 0, 0, 0);
-                o[b][db + 1] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v1), as_bf16x8(pf[b]), o[b][db + 1], 0, 0, 0);
-            }
-#pragma unroll
-            for (int b = 0; b < NQB; ++b) {
-                o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v0), as_bf16x8(pl[b]), o[b][db], 0, 0, 0);
-                o[b][db + 1] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v1), as_bf16x8(pl[b]), o[b][db + 1], 0, 0, 0);
-            }
-        };
-        // masked tile: nonfinite values become 0 (exponent all ones -> zero)
-        // and an indicator product records which (dim, vector) outputs saw
-        // one among their visible keys
-        uint64_t bad = 0;
-        auto vclean = [&](u32x4_t vf, int db) {
-            u32x4_t ind;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t x = vf[w];
-                const bool nlo = (x & 0x7F80u) == 0x7F80u;
-                const bool nhi = (x & 0x7F800000u) == 0x7F800000u;
-                vf[w] = (nlo ? 0u : (x & 0xFFFFu)) | (nhi ? 0u : (x & 0xFFFF0000u));
-                ind[w] = (nlo ? 0x3F80u : 0u) | (nhi ? 0x3F800000u : 0u);
-                bad |= __builtin_amdgcn_ballot_w64(nlo || nhi);
-            }
-            if (bad != 0) {
-                // count of visible nonfinite values per (dim, vector)
-#pragma unroll
+            if (need != 0) {
+    #pragma unroll
                 for (int b = 0; b < NQB; ++b) {
-                    u32x4_t visf;
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const int ka = kt + (w >> 1) * 16 + lg * 4 + (w & 1) * 2;
-                        const bool v0 = row_sees<MASK>(ka, lim[b], tb, anc[b]);
-                        const bool v1 = row_sees<MASK>(ka + 1, lim[b], tb, anc[b]);
-                        visf[w] = (v0 ? 0x3F80u : 0u) | (v1 ? 0x3F800000u : 0u);
+                    const bool up = tmax[b] > m[b];
+                    const float alpha = up ? exp2_fast((m[b] - tmax[b]) * c) : 1.0f;
+                    m[b] = up ? tmax[b] : m[b];
+                    mc[b] = up ? tmax[b] * c : mc[b];
+                    thr[b] = up ? tmax[b] + lazy : thr[b];
+                    lsum[b] *= alpha;
+    #pragma unroll
+                    for (int d = 0; d < DBG; ++d)
+                        o[b][d] *= alpha;
+                }
+            }
+    #pragma unroll
+            for (int b = 0; b < NQB; ++b) {
+                float pe[8];
+    #pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        pe[kb * 4 + e] = exp2_fast(fmaf(s[b][kb][e], c, -mc[b]));
+                // p = hi + lo, both bf16: the value product takes the two parts, so
+                // the weights keep about 16 significant bits instead of 8
+                float pr[8];
+    #pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    pf[b][w] = pack_bf16(pe[2 * w], pe[2 * w + 1]);
+                    pr[2 * w] = pe[2 * w] - bf16_lo(pf[b][w]);
+                    pr[2 * w + 1] = pe[2 * w + 1] - bf16_hi(pf[b][w]);
+                }
+    #pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    pl[b][w] = pack_bf16(pr[2 * w], pr[2 * w + 1]);
+                lsum[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, as_bf16x8(pf[b]), lsum[b], 0, 0, 0);
+                lsum[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, as_bf16x8(pl[b]), lsum[b], 0, 0, 0);
+            }
+
+            // -- values: O^T += V^T P^T per 16-dim block.  V^T fragment of lane
+            // (lg, lc): dims 16 db + lc, keys 4 lg .. + 4 and 16 + 4 lg .. + 4,
+            // by two transposed reads of 4 x 16 blocks
+            auto vread = [&](int db) {
+                // the 16 lanes of group lg read the 4 x 16 block of keys
+                // 4 lg .. + 4 (resp. 16 + 4 lg ..), dims 16 db .. + 16: lane
+                // i of the group reads key 4 lg + i / 4, dims 16 db + 4 (i % 4) .. + 4
+                const int key0 = lg * 4 + (lc >> 2);
+                const int dim = db * 16 + (lc & 3) * 4;
+                const uint32_t o0 = unit_off<D>(key0, dim >> 3) + (dim & 7) * 2;
+                const uint32_t o1 = unit_off<D>(key0 + 16, dim >> 3) + (dim & 7) * 2;
+                const i16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(vt_lds + o0));
+                const i16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(vt_lds + o1));
+                return u32x4_t{(uint32_t)(uint16_t)h0[0] | ((uint32_t)(uint16_t)h0[1] << 16),
+                               (uint32_t)(uint16_t)h0[2] | ((uint32_t)(uint16_t)h0[3] << 16),
+                               (uint32_t)(uint16_t)h1[0] | ((uint32_t)(uint16_t)h1[1] << 16),
+                               (uint32_t)(uint16_t)h1[2] | ((uint32_t)(uint16_t)h1[3] << 16)};
+            };
+            // the products of two dim blocks: the rounded and the remainder
+            // terms of one block are not back to back (independent chains)
+            auto pv2 = [&](int db, const u32x4_t &v0, const u32x4_t &v1) {
+    #pragma unroll
+                for (int b = 0; b < NQB; ++b) {
+                    o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v0), as_bf16x8(pf[b]), o[b][db], 0, 0, 0);
+                    o[b][db + 1] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v1), as_bf16x8(pf[b]), o[b][db + 1], 0, 0, 0);
+                }
+    #pragma unroll
+                for (int b = 0; b < NQB; ++b) {
+                    o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v0), as_bf16x8(pl[b]), o[b][db], 0, 0, 0);
+                    o[b][db + 1] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v1), as_bf16x8(pl[b]), o[b][db + 1], 0, 0, 0);
+                }
+            };
+            // masked tile: nonfinite values become 0 (exponent all ones -> zero)
+            // and an indicator product records which (dim, vector) outputs saw
+            // one among their visible keys
+            uint64_t bad = 0;
+            auto vclean = [&](u32x4_t vf, int db) {
+                u32x4_t ind;
+    #pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t x = vf[w];
+                    const bool nlo = (x & 0x7F80u) == 0x7F80u;
+                    const bool nhi = (x & 0x7F800000u) == 0x7F800000u;
+                    vf[w] = (nlo ? 0u : (x & 0xFFFFu)) | (nhi ? 0u : (x & 0xFFFF0000u));
+                    ind[w] = (nlo ? 0x3F80u : 0u) | (nhi ? 0x3F800000u : 0u);
+                    bad |= __builtin_amdgcn_ballot_w64(nlo || nhi);
+                }
+                if (bad != 0) {
+                    // count of visible nonfinite values per (dim, vector)
+    #pragma unroll
+                    for (int b = 0; b < NQB; ++b) {
+                        u32x4_t visf;
+    #pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            const int ka = kt + (w >> 1) * 16 + lg * 4 + (w & 1) * 2;
+                            const bool v0 = row_sees<MASK>(ka, lim[b], tb, anc[b]);
+                            const bool v1 = row_sees<MASK>(ka + 1, lim[b], tb, anc[b]);
+                            visf[w] = (v0 ? 0x3F80u : 0u) | (v1 ? 0x3F800000u : 0u);
+                        }
+                        const f32x4_t cnt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            as_bf16x8(ind), as_bf16x8(visf), f32x4_t{0, 0, 0, 0}, 0, 0, 0);
+    #pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int bit = db * 4 + e;
+                            if (cnt[e] > 0.0f)
+                                nanmask[b][bit >> 5] |= 1u << (bit & 31);
+                        }
                     }
-                    const f32x4_t cnt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        as_bf16x8(ind), as_bf16x8(visf), f32x4_t{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
+                }
+                return vf;
+            };
+            // The fragments of the next group of dim blocks are read while this
+            // group's products run (a double buffer of VG fragments; the
+            // scheduling barriers keep the compiler from reading further ahead
+            // than the registers allow), so no product waits on its own read.
+            // (local dim block j is dim block db0 + j)
+            constexpr int VG = D == 256 ? 2 : (DBG < 4 ? DBG : 4);
+            u32x4_t cur[VG], nxt[VG];
+    #pragma unroll
+            for (int j = 0; j < VG; ++j)
+                cur[j] = vread(db0 + j);
+    #pragma unroll
+            for (int g0 = 0; g0 < DBG; g0 += VG) {
+                if (g0 + VG < DBG) {
+    #pragma unroll
+                    for (int j = 0; j < VG; ++j)
+                        nxt[j] = vread(db0 + g0 + VG + j);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int j = 0; j < VG; j += 2) {
+                    u32x4_t v0 = cur[j], v1 = cur[j + 1];
+                    if (!full) {
+                        v0 = vclean(v0, g0 + j);
+                        v1 = vclean(v1, g0 + j + 1);
+                    }
+                    pv2(g0 + j, v0, v1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (g0 + VG < DBG) {
+    #pragma unroll
+                    for (int j = 0; j < VG; ++j)
+                        cur[j] = nxt[j];
+                }
+            }
+        }
+        if (page_bad) {
+            report(p.err, TF_ERR_BAD_PAGE);
+    #pragma unroll
+            for (int b = 0; b < NQB; ++b)
+                lsum[b] = f32x4_t{NAN, NAN, NAN, NAN};
+        }
+
+        // ---- write: lane (lg, lc) holds dims 16 (db0 + db) + 4 lg .. + 4 of vector lc
+    #pragma unroll
+        for (int b = 0; b < NQB; ++b) {
+            float a, bb;
+            swap16(lo[b], a, bb);
+            float lw = min2(a, bb);
+            swap32(lw, a, bb);
+            lw = min2(a, bb);
+            if (!qvalid[b])
+                continue;
+            const int qv = qv0 + b * 16 + lc;
+            const int r = qv / group;
+            const int h = g * group + qv % group;
+            const float ll = lsum[b][0];
+            const bool nan_out = __builtin_isnan(ll) || lw == -INFINITY || errbits != 0;
+            if (p.split_keys > 0) {
+                if (!parts_ok)
+                    continue;
+                const int64_t recno = partial_offset + ((int64_t)r * p.hq + h) * n_splits + t;
+                float *rec = p.partials + recno * (D + 4);
+                if (lg == 0 && dg == 0)
+                    *reinterpret_cast<float4 *>(rec) =
+                        make_float4(nan_out ? NAN : m[b] * (c * kLn2), nan_out ? NAN : ll, 0.0f, 0.0f);
+    #pragma unroll
+                for (int db = 0; db < DBG; ++db) {
+                    float4 v;
+                    float *vp = &v.x;
+    #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int bit = db * 4 + e;
-                        if (cnt[e] > 0.0f)
-                            nanmask[b][bit >> 5] |= 1u << (bit & 31);
+                        const bool nb = (nanmask[b][bit >> 5] >> (bit & 31)) & 1u;
+                        vp[e] = (nan_out || nb) ? NAN : o[b][db][e];
                     }
+                    *reinterpret_cast<float4 *>(rec + 4 + (db0 + db) * 16 + lg * 4) = v;
                 }
-            }
-            return vf;
-        };
-        // The fragments of the next group of dim blocks are read while this
-        // group's products run (a double buffer of VG fragments; the
-        // scheduling barriers keep the compiler from reading further ahead
-        // than the registers allow), so no product waits on its own read.
-        constexpr int VG = D == 256 ? 2 : (DB < 4 ? DB : 4);
-        u32x4_t cur[VG], nxt[VG];
-#pragma unroll
-        for (int j = 0; j < VG; ++j)
-            cur[j] = vread(j);
-#pragma unroll
-        for (int g0 = 0; g0 < DB; g0 += VG) {
-            if (g0 + VG < DB) {
-#pragma unroll
-                for (int j = 0; j < VG; ++j)
-                    nxt[j] = vread(g0 + VG + j);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < VG; j += 2) {
-                u32x4_t v0 = cur[j], v1 = cur[j + 1];
-                if (!full) {
-                    v0 = vclean(v0, g0 + j);
-                    v1 = vclean(v1, g0 + j + 1);
+            } else {
+                uint16_t *dst = p.out + ((size_t)(row_offset + r) * p.hq + h) * D;
+    #pragma unroll
+                for (int db = 0; db < DBG; ++db) {
+                    uint16_t hb[4];
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int bit = db * 4 + e;
+                        const bool nb = (nanmask[b][bit >> 5] >> (bit & 31)) & 1u;
+                        hb[e] = (nan_out || nb) ? kBf16NaN : bf16_out(o[b][db][e] / ll);
+                    }
+                    *reinterpret_cast<uint2 *>(dst + (db0 + db) * 16 + lg * 4) =
+                        make_uint2((uint32_t)hb[0] | ((uint32_t)hb[1] << 16), (uint32_t)hb[2] | ((uint32_t)hb[3] << 16));
                 }
-                pv2(g0 + j, v0, v1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if (g0 + VG < DB) {
-#pragma unroll
-                for (int j = 0; j < VG; ++j)
-                    cur[j] = nxt[j];
             }
         }
-    }
-    if (page_bad) {
-        report(p.err, TF_ERR_BAD_PAGE);
-#pragma unroll
-        for (int b = 0; b < NQB; ++b)
-            lsum[b] = f32x4_t{NAN, NAN, NAN, NAN};
-    }
-
-    // ---- write: lane (lg, lc) holds dims 16 db + 4 lg .. + 4 of vector lc
-#pragma unroll
-    for (int b = 0; b < NQB; ++b) {
-        float a, bb;
-        swap16(lo[b], a, bb);
-        float lw = min2(a, bb);
-        swap32(lw, a, bb);
-        lw = min2(a, bb);
-        if (!qvalid[b])
-            continue;
-        const int qv = qv0 + b * 16 + lc;
-        const int r = qv / group;
-        const int h = g * group + qv % group;
-        const float ll = lsum[b][0];
-        const bool nan_out = __builtin_isnan(ll) || lw == -INFINITY || errbits != 0;
-        if (p.split_keys > 0) {
-            if (!parts_ok)
-                continue;
-            const int64_t recno = partial_offset + ((int64_t)r * p.hq + h) * n_splits + t;
-            float *rec = p.partials + recno * (D + 4);
-            if (lg == 0)
-                *reinterpret_cast<float4 *>(rec) =
-                    make_float4(nan_out ? NAN : m[b] * (c * kLn2), nan_out ? NAN : ll, 0.0f, 0.0f);
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                float4 v;
-                float *vp = &v.x;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int bit = db * 4 + e;
-                    const bool nb = (nanmask[b][bit >> 5] >> (bit & 31)) & 1u;
-                    vp[e] = (nan_out || nb) ? NAN : o[b][db][e];
-                }
-                *reinterpret_cast<float4 *>(rec + 4 + db * 16 + lg * 4) = v;
-            }
-        } else {
-            uint16_t *dst = p.out + ((size_t)(row_offset + r) * p.hq + h) * D;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                uint16_t hb[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int bit = db * 4 + e;
-                    const bool nb = (nanmask[b][bit >> 5] >> (bit & 31)) & 1u;
-                    hb[e] = (nan_out || nb) ? kBf16NaN : bf16_out(o[b][db][e] / ll);
-                }
-                *reinterpret_cast<uint2 *>(dst + db * 16 + lg * 4) =
-                    make_uint2((uint32_t)hb[0] | ((uint32_t)hb[1] << 16), (uint32_t)hb[2] | ((uint32_t)hb[3] << 16));
-            }
-        }
-    }
+    };
+    if (kw == 1)
+        body(IntC<1>{});
+    else if (kw == 2)
+        body(IntC<2 <= KW_MAX ? 2 : 1>{});
+    else if (kw == 4)
+        body(IntC<4 <= KW_MAX ? 4 : 1>{});
+    else
+        body(IntC<8 <= KW_MAX ? 8 : 1>{});
     if (threadIdx.x == 0 && g == 0 && t == 0 && qt == 0)
         report(p.err, errbits);
 }
