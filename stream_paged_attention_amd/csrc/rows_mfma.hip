@@ -388,17 +388,17 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
         f32x4_t o[NQB][DBG];   // o[b][j]: dim block db0 + j
         f32x4_t lsum[NQB];   // ones-block product: every element is l of the lane's vector
         uint32_t nanmask[NQB][(DBG * 4 + 31) / 32];
-    #pragma unroll
+#pragma unroll
         for (int b = 0; b < NQB; ++b) {
             m[b] = -INFINITY;
             mc[b] = 0.0f;
             thr[b] = -INFINITY;
             lo[b] = INFINITY;
             lsum[b] = f32x4_t{0, 0, 0, 0};
-    #pragma unroll
+#pragma unroll
             for (int d = 0; d < DBG; ++d)
                 o[b][d] = f32x4_t{0, 0, 0, 0};
-    #pragma unroll
+#pragma unroll
             for (int w = 0; w < (DBG * 4 + 31) / 32; ++w)
                 nanmask[b][w] = 0;
         }
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
         if (n_tiles > 0)
             load_pids(0);
         wait_vm<0>();
-    #pragma unroll
+#pragma unroll
         for (int u = 0; u < PD; ++u)
             if (u < n_tiles)
                 issue(u, u);
@@ -444,18 +444,18 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
             // (even and odd dim steps accumulate apart: four independent
             // product chains per vector block keep the matrix pipe busy)
             f32x4_t s[NQB][2], s2[NQB][2];
-    #pragma unroll
+#pragma unroll
             for (int b = 0; b < NQB; ++b)
                 s[b][0] = s[b][1] = s2[b][0] = s2[b][1] = f32x4_t{0, 0, 0, 0};
-    #pragma unroll
+#pragma unroll
             for (int ks = 0; ks < KS; ks += 2) {
-    #pragma unroll
+#pragma unroll
                 for (int h = 0; h < 2; ++h) {
-    #pragma unroll
+#pragma unroll
                     for (int kb = 0; kb < 2; ++kb) {
                         const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(
                             kt_lds + unit_off<D>(kb * 16 + lc, (ks + h) * 4 + lg));
-    #pragma unroll
+#pragma unroll
                         for (int b = 0; b < NQB; ++b) {
                             f32x4_t &acc = h ? s2[b][kb] : s[b][kb];
                             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[b][ks + h]),
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
                     }
                 }
             }
-    #pragma unroll
+#pragma unroll
             for (int b = 0; b < NQB; ++b) {
                 s[b][0] += s2[b][0];
                 s[b][1] += s2[b][1];
@@ -474,12 +474,12 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
             u32x4_t pf[NQB], pl[NQB];   // P^T in bf16: rounded value and its remainder
             uint64_t need = 0;
             float tmax[NQB];
-    #pragma unroll
+#pragma unroll
             for (int b = 0; b < NQB; ++b) {
                 float mx = -INFINITY;
-    #pragma unroll
+#pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         float x = s[b][kb][e];
                         if (!full) {
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
                 need |= __builtin_amdgcn_ballot_w64(mx > thr[b]);
             }
             if (need != 0) {
-    #pragma unroll
+#pragma unroll
                 for (int b = 0; b < NQB; ++b) {
                     const bool up = tmax[b] > m[b];
                     const float alpha = up ? exp2_fast((m[b] - tmax[b]) * c) : 1.0f;
@@ -511,29 +511,29 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
                     mc[b] = up ? tmax[b] * c : mc[b];
                     thr[b] = up ? tmax[b] + lazy : thr[b];
                     lsum[b] *= alpha;
-    #pragma unroll
+#pragma unroll
                     for (int d = 0; d < DBG; ++d)
                         o[b][d] *= alpha;
                 }
             }
-    #pragma unroll
+#pragma unroll
             for (int b = 0; b < NQB; ++b) {
                 float pe[8];
-    #pragma unroll
+#pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < 4; ++e)
                         pe[kb * 4 + e] = exp2_fast(fmaf(s[b][kb][e], c, -mc[b]));
                 // p = hi + lo, both bf16: the value product takes the two parts, so
                 // the weights keep about 16 significant bits instead of 8
                 float pr[8];
-    #pragma unroll
+#pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     pf[b][w] = pack_bf16(pe[2 * w], pe[2 * w + 1]);
                     pr[2 * w] = pe[2 * w] - bf16_lo(pf[b][w]);
                     pr[2 * w + 1] = pe[2 * w + 1] - bf16_hi(pf[b][w]);
                 }
-    #pragma unroll
+#pragma unroll
                 for (int w = 0; w < 4; ++w)
                     pl[b][w] = pack_bf16(pr[2 * w], pr[2 * w + 1]);
                 lsum[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, as_bf16x8(pf[b]), lsum[b], 0, 0, 0);
@@ -563,13 +563,13 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
             // the products of two dim blocks: the rounded and the remainder
             // terms of one block are not back to back (independent chains)
             auto pv2 = [&](int db, const u32x4_t &v0, const u32x4_t &v1) {
-    #pragma unroll
+#pragma unroll
                 for (int b = 0; b < NQB; ++b) {
                     o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v0), as_bf16x8(pf[b]), o[b][db], 0, 0, 0);
                     o[b][db + 1] =
                         __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v1), as_bf16x8(pf[b]), o[b][db + 1], 0, 0, 0);
                 }
-    #pragma unroll
+#pragma unroll
                 for (int b = 0; b < NQB; ++b) {
                     o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v0), as_bf16x8(pl[b]), o[b][db], 0, 0, 0);
                     o[b][db + 1] =
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
             uint64_t bad = 0;
             auto vclean = [&](u32x4_t vf, int db) {
                 u32x4_t ind;
-    #pragma unroll
+#pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const uint32_t x = vf[w];
                     const bool nlo = (x & 0x7F80u) == 0x7F80u;
@@ -593,10 +593,10 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
                 }
                 if (bad != 0) {
                     // count of visible nonfinite values per (dim, vector)
-    #pragma unroll
+#pragma unroll
                     for (int b = 0; b < NQB; ++b) {
                         u32x4_t visf;
-    #pragma unroll
+#pragma unroll
                         for (int w = 0; w < 4; ++w) {
                             const int ka = kt + (w >> 1) * 16 + lg * 4 + (w & 1) * 2;
                             const bool v0 = row_sees<MASK>(ka, lim[b], tb, anc[b]);
@@ -605,7 +605,7 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
                         }
                         const f32x4_t cnt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             as_bf16x8(ind), as_bf16x8(visf), f32x4_t{0, 0, 0, 0}, 0, 0, 0);
-    #pragma unroll
+#pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int bit = db * 4 + e;
                             if (cnt[e] > 0.0f)
@@ -622,18 +622,22 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
             // (local dim block j is dim block db0 + j)
             constexpr int VG = D == 256 ? 2 : (DBG < 4 ? DBG : 4);
             u32x4_t cur[VG], nxt[VG];
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < VG; ++j)
                 cur[j] = vread(db0 + j);
-    #pragma unroll
+            // the value products run at raised wave priority, so that the
+            // SIMD's arbiter favours the wave in this phase over one in its
+            // softmax (about 1 % faster on all three MFMA workloads)
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
             for (int g0 = 0; g0 < DBG; g0 += VG) {
                 if (g0 + VG < DBG) {
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < VG; ++j)
                         nxt[j] = vread(db0 + g0 + VG + j);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < VG; j += 2) {
                     u32x4_t v0 = cur[j], v1 = cur[j + 1];
                     if (!full) {
@@ -644,21 +648,22 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (g0 + VG < DBG) {
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < VG; ++j)
                         cur[j] = nxt[j];
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         if (page_bad) {
             report(p.err, TF_ERR_BAD_PAGE);
-    #pragma unroll
+#pragma unroll
             for (int b = 0; b < NQB; ++b)
                 lsum[b] = f32x4_t{NAN, NAN, NAN, NAN};
         }
 
         // ---- write: lane (lg, lc) holds dims 16 (db0 + db) + 4 lg .. + 4 of vector lc
-    #pragma unroll
+#pragma unroll
         for (int b = 0; b < NQB; ++b) {
             float a, bb;
             swap16(lo[b], a, bb);
@@ -680,11 +685,11 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
                 if (lg == 0 && dg == 0)
                     *reinterpret_cast<float4 *>(rec) =
                         make_float4(nan_out ? NAN : m[b] * (c * kLn2), nan_out ? NAN : ll, 0.0f, 0.0f);
-    #pragma unroll
+#pragma unroll
                 for (int db = 0; db < DBG; ++db) {
                     float4 v;
                     float *vp = &v.x;
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int bit = db * 4 + e;
                         const bool nb = (nanmask[b][bit >> 5] >> (bit & 31)) & 1u;
@@ -694,10 +699,10 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
                 }
             } else {
                 uint16_t *dst = p.out + ((size_t)(row_offset + r) * p.hq + h) * D;
-    #pragma unroll
+#pragma unroll
                 for (int db = 0; db < DBG; ++db) {
                     uint16_t hb[4];
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int bit = db * 4 + e;
                         const bool nb = (nanmask[b][bit >> 5] >> (bit & 31)) & 1u;
