@@ -97,6 +97,19 @@ def test_batched_equals_per_segment(workloads, name):
     assert np.array_equal(batched, single), f"{name}: batched launch differs from per-segment"
 
 
+def test_rotated_grid_batched_equals_per_segment(gpu):
+    # 2 kv heads x 4 segments: the batched matrix-core launch rotates segments
+    # by split, each single-segment launch does not; the bytes must agree
+    keys = [5000, 300, 2100, 64]
+    w = synth.make_workload("rot", synth.KIND_PAGED, 16, 2, 128, [40, 3, 17, 1], keys, seed=44,
+                            page_size=32, pool_pages=sum(-(-k // 32) for k in keys) + 5, split_keys=512)
+    dw = launch.DeviceWorkload(w, gpu)
+    dw.run()
+    batched = dw.output()
+    assert np.array_equal(batched, dw.run_per_segment()), "rotated grid: batched differs from per-segment"
+    assert dw.error_word() == 0
+
+
 def test_repeats_are_byte_identical(workloads):
     w, dw = workloads("decode16")
     outs = []
@@ -181,6 +194,9 @@ SHAPES = [
     ("paged", 128, 32, 8, [1, 1], [131072, 3000], 512),   # a long decode context, 256 splits
     ("paged", 128, 8, 2, [1, 3], [20000, 20000], 32),    # 625 splits, both rows kernels
     ("contig", 64, 64, 1, [1], [2100], 32),              # 64 query heads on one kv head (MFMA)
+    # hkv * n_segments a multiple of 8: the matrix-core grid rotates segments by split
+    ("paged", 128, 16, 2, [40, 3, 17, 1], [5000, 300, 2100, 64], 512),   # 1 to 5 query tiles
+    ("ring", 256, 16, 4, [33, 2], [3000, 1500], 256),
 ]
 
 
