@@ -7,8 +7,10 @@
 // Work item = one workgroup = (segment, kv head g, split t, query tile).  A
 // query tile is QB query vectors (row-major over the segment's rows, the
 // group's query heads fastest); each of the NW waves owns NQB blocks of 16.
-// Which workgroup serves which item is set by grid_cell below, so that the
-// shader engines get even shares of the keys.
+// A tile with fewer blocks than waves (verify and drafter rounds) gives each
+// block several waves, which split its output dims.  Which workgroup serves
+// which item is set by grid_cell below, so that the shader engines get even
+// shares of the keys.
 //
 // Per 32-key tile, all from LDS, each wave computes
 //     S^T = K Q^T          (v_mfma_f32_16x16x32_bf16, A = K rows, B = Q^T)
