@@ -9,8 +9,8 @@
 // group's query heads fastest); each of the NW waves owns NQB blocks of 16.
 // A tile with fewer blocks than waves (verify and drafter rounds) gives each
 // block several waves, which split its output dims.  Which workgroup serves
-// which item is set by grid_cell below, so that the shader engines get even
-// shares of the keys.
+// which item is set by grid_cell (grid_cell.hpp), so that the shader
+// engines get even shares of the keys.
 //
 // Per 32-key tile, all from LDS, each wave computes
 //     S^T = K Q^T          (v_mfma_f32_16x16x32_bf16, A = K rows, B = Q^T)
@@ -38,6 +38,7 @@
 // which (dimension, query vector) outputs saw a nonfinite value among their
 // visible keys; those are written as NaN (the NaN rule for values).
 #include "device.hpp"
+#include "grid_cell.hpp"
 
 namespace tfa {
 
@@ -143,44 +144,6 @@ __device__ __forceinline__ void wait_tiles(int newer)
         else
             wait_tiles<L, MAXN - 1>(newer);
     }
-}
-
-// Work item of workgroup i.  The dispatcher sends workgroup i to XCD i % 8
-// and, inside the XCD, to its four shader engines in turn ((i / 8) % 4),
-// in order: a workgroup whose engine is full holds back the ones after it,
-// even those bound for an engine with room.  With one or two workgroups a
-// CU, the items a residue of i mod 32 collects should therefore hold about
-// the same number of keys.  In the plain order (kv head fastest, then
-// segment, split, query tile) the residue of item (g, s, t) is
-// g + hkv * s + hkv * n_segments * t (mod 32): when hkv * n_segments is a
-// multiple of 8 the split index moves it little or not at all, and every
-// split of a long segment queues on one engine while the engines of short
-// segments idle.  In that case the segment index is rotated by the split
-// index (workgroup column s serves segment (s - t) mod n_segments), so that
-// each engine sees every segment.  Otherwise the plain order already spreads
-// a segment's splits over the engines and is kept.  Either way the query
-// tiles of one (kv head, segment, split) sit hkv * n_segments * n_split_max
-// workgroups apart, on one XCD when that is a multiple of 8.
-struct Cell {
-    int g, seg, t, qt;
-};
-
-__device__ __forceinline__ Cell grid_cell(int i, int hkv, int n_segments, int n_split_max)
-{
-    Cell x;
-    x.g = i % hkv;
-    int r = i / hkv;
-    const int col = r % n_segments;
-    r /= n_segments;
-    x.t = r % n_split_max;
-    x.qt = r / n_split_max;
-    int seg = col;
-    if ((hkv * n_segments) % 8 == 0) {
-        seg = (col - x.t) % n_segments;
-        seg += seg < 0 ? n_segments : 0;
-    }
-    x.seg = seg;
-    return x;
 }
 
 template <int D, int KIND, int MASK>
