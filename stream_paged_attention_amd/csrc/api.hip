@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <vector>
 
 #include "device.hpp"
@@ -80,6 +81,21 @@ int check_args(const tf_attn_args *a, bool need_partials)
             return TF_E_INVALID;
     }
     return TF_OK;
+}
+
+// Whether the product of the (non-negative) factors stays at or below limit,
+// without overflowing on the way.
+bool product_fits(std::initializer_list<int64_t> factors, int64_t limit)
+{
+    int64_t x = 1;
+    for (const int64_t f : factors) {
+        if (f == 0)
+            return true;
+        if (f < 0 || x > limit / f)
+            return false;
+        x *= f;
+    }
+    return true;
 }
 
 tfa::RowsParams make_params(const tf_attn_args *a)
@@ -223,7 +239,7 @@ int tf_attn_rows(const tf_attn_args *a, hipStream_t stream)
         return TF_OK;
     tfa::RowsParams p = make_params(a);
     // one block per (split, segment, kv head), in a one-dimensional grid
-    if ((int64_t)p.n_split_max * p.n_segments * p.hkv > (int64_t)INT32_MAX / 256)
+    if (!product_fits({p.n_split_max, p.n_segments, p.hkv}, (int64_t)INT32_MAX / 256))
         return TF_E_UNSUPPORTED;
     // Segments with at most kMfmaMinQ query vectors per kv head (decode,
     // short verify) run on the VALU kernel, the others on the MFMA kernel;
@@ -231,7 +247,7 @@ int tf_attn_rows(const tf_attn_args *a, hipStream_t stream)
     const int64_t nq_max = (int64_t)a->max_rows * p.group;
     const int64_t n_qt = (nq_max + tfa::mfma_query_tile(a->head_dim) - 1) / tfa::mfma_query_tile(a->head_dim);
     if (nq_max > p.mfma_min_q &&
-        n_qt * p.n_split_max * p.n_segments * p.hkv > (int64_t)INT32_MAX / 512)
+        !product_fits({n_qt, p.n_split_max, p.n_segments, p.hkv}, (int64_t)INT32_MAX / 512))
         return TF_E_UNSUPPORTED;
     if (a->min_rows > 0 && (int64_t)a->min_rows * p.group > p.mfma_min_q) {
         // every segment has many query vectors: no decode launch, and the

@@ -154,6 +154,10 @@ def _args(**kw):
     (dict(mask=binding.TF_MASK_TREE, tree=0x50004), binding.TF_E_INVALID),      # misaligned
     (dict(mask=binding.TF_MASK_TREE, tree=0x50000, max_rows=65, max_keys=100),
      binding.TF_E_INVALID),                                                     # more than 64 rows
+    # grids past the launch limit are refused before any launch
+    (dict(split=32, max_keys=2**31 - 1, partials=0x10000, partials_bytes=1 << 40), binding.TF_E_UNSUPPORTED),
+    (dict(hq=2**30, hkv=2**30), binding.TF_E_UNSUPPORTED),
+    (dict(hq=2**30, hkv=1, max_rows=2, max_keys=100), binding.TF_E_UNSUPPORTED),   # matrix-core grid
 ])
 def test_rows_refuses_bad_scalars_without_launching(kw, rc):
     # stream 0 and fake pointers: a refused call must return before any launch
