@@ -397,3 +397,34 @@ def test_argmax_small_cases(gpu):
     rids2, rflags2 = oracle.argmax(wide, vocab=9001)
     np.testing.assert_array_equal(ids2, rids2)
     np.testing.assert_array_equal(flags2, rflags2)
+
+
+def _vocab_edge_rows(vocab, seed):
+    """Rows for one vocabulary size: random, ties at both ends, across the
+    8192-logit chunk boundary and at the last chunk's first id, all equal,
+    all NaN, and a +inf after a NaN."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = synth.normal_logits(rng, 8, vocab)
+    synth.plant_tie(x, 1, sorted({0, vocab - 1}))
+    if vocab > 8192:
+        synth.plant_tie(x, 2, [8191, 8192])
+        last = (vocab - 1) // 8192 * 8192
+        synth.plant_tie(x, 3, sorted({5, last}))
+    else:
+        synth.plant_tie(x, 2, sorted({vocab // 2, vocab - 1}))
+    x[4, :] = synth.f32_to_bf16_bits(np.float32(-3.0))
+    x[5, :] = synth.BF16_NAN
+    x[6, 0] = synth.BF16_NAN
+    x[6, vocab - 1] = synth.BF16_POS_INF
+    x[7, :] = synth.BF16_NEG_INF
+    return x
+
+
+@pytest.mark.parametrize("vocab", [1, 2, 7, 64, 255, 256, 257, 8191, 8192, 8193, 16384, 24577])
+def test_argmax_vocab_edges(gpu, vocab):
+    print(f"argmax vocab {vocab}", flush=True)
+    x = _vocab_edge_rows(vocab, seed=vocab)
+    ids, flags = launch.argmax(x)
+    rids, rflags = oracle.argmax(x)
+    np.testing.assert_array_equal(ids, rids)
+    np.testing.assert_array_equal(flags, rflags)
