@@ -13,7 +13,7 @@
 namespace tfa {
 hipError_t launch_rows_valu(const RowsParams &p, int head_dim, int kind, hipStream_t st);
 hipError_t launch_rows_mfma(const RowsParams &p, int head_dim, int kind, int max_q, hipStream_t st);
-int mfma_query_tile(int head_dim);
+int mfma_query_tile(int head_dim, int64_t max_q);
 hipError_t launch_merge(const RowsParams &p, int head_dim, int max_rows, hipStream_t st);
 hipError_t launch_argmax(const uint16_t *logits, int n_rows, int vocab, int64_t row_stride,
                          int32_t *ids, uint8_t *flags, void *workspace, hipStream_t st);
@@ -245,7 +245,8 @@ int tf_attn_rows(const tf_attn_args *a, hipStream_t stream)
     // short verify) run on the VALU kernel, the others on the MFMA kernel;
     // the choice depends on the segment alone.
     const int64_t nq_max = (int64_t)a->max_rows * p.group;
-    const int64_t n_qt = (nq_max + tfa::mfma_query_tile(a->head_dim) - 1) / tfa::mfma_query_tile(a->head_dim);
+    const int qb = tfa::mfma_query_tile(a->head_dim, nq_max);
+    const int64_t n_qt = (nq_max + qb - 1) / qb;
     if (nq_max > p.mfma_min_q &&
         !product_fits({n_qt, p.n_split_max, p.n_segments, p.hkv}, (int64_t)INT32_MAX / 512))
         return TF_E_UNSUPPORTED;

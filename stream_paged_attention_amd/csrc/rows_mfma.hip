@@ -31,6 +31,15 @@
 // reading one unit column hit distinct banks.  NBUF tile buffers: NBUF - 1
 // tiles in flight while one is multiplied, one barrier per tile.
 //
+// Two shapes at head dim 256.  Prompt chunks: 8 waves (128 query vectors) a
+// workgroup with four tile buffers (128 KB of LDS), one workgroup a CU, so
+// each staged tile serves 128 vectors.  Launches whose segments all have at
+// most 64 query vectors per kv head (verify rounds): 4 waves a workgroup
+// with two tile buffers (64 KB) and registers held to two waves a SIMD, so
+// that two workgroups share a CU and run out of step; with one 8-wave
+// workgroup a CU those launches ran their work items in two to three rounds
+// of barrier-locked waves.
+//
 // Masking (causal rows, a tree's block, split end, keys past the count)
 // happens on the scores.  A masked key's value must add exactly nothing, but 0 * NaN = NaN
 // on the matrix core: in tiles that mask anything, nonfinite value elements
@@ -51,9 +60,11 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 constexpr int kKT = 32;                // keys per tile
 constexpr float kMLazy = 8.0f;         // log2 of the largest weight a stale reference may give
 
-template <int D>
+// SMALL: the head-dim-256 shape for launches of at most 64 query vectors
+// per kv head (it changes nothing below 256)
+template <int D, bool SMALL = false>
 struct MGeo {
-    static constexpr int NW = D == 256 ? 8 : 4;       // waves per workgroup
+    static constexpr int NW = D == 256 && !SMALL ? 8 : 4;   // waves per workgroup
     static constexpr int KS = D / 32;                 // 32-dim steps of the score product
     static constexpr int DB = D / 16;                 // 16-dim blocks of the output
     static constexpr int UPR = D / 8;                 // 16-byte units per key row
@@ -63,8 +74,8 @@ struct MGeo {
     static constexpr int LOADS = TILE / 1024 / NW;    // 1 KB wave loads per wave per tile (K or V)
     // LDS tile buffers (K and V): NBUF - 1 tiles in flight while one is
     // multiplied; 128 KB of LDS at D 256 (one workgroup of 8 waves a CU),
-    // 64 KB below (two workgroups of 4 waves)
-    static constexpr int NBUF = D == 256 ? 4 : (D == 128 ? 4 : 8);
+    // 64 KB for the small D 256 shape and below (two workgroups of 4 waves)
+    static constexpr int NBUF = D == 256 ? (SMALL ? 2 : 4) : (D == 128 ? 4 : 8);
     static constexpr int PD = NBUF - 1;               // prefetch distance in tiles
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == TILE, "tile must split into 1 KB wave loads");
 };
@@ -146,10 +157,11 @@ __device__ __forceinline__ void wait_tiles(int newer)
     }
 }
 
-template <int D, int KIND, int MASK>
-__global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams p)
+template <int D, int KIND, int MASK, bool SMALL>
+__global__ __launch_bounds__((64 * MGeo<D, SMALL>::NW))
+__attribute__((amdgpu_waves_per_eu(SMALL ? 2 : 1))) void rows_mfma_kernel(RowsParams p)
 {
-    using G = MGeo<D>;
+    using G = MGeo<D, SMALL>;
     constexpr int KS = G::KS, DB = G::DB, NQB = G::NQB, QB = G::QB, LOADS = G::LOADS, NW = G::NW;
     constexpr int NBUF = G::NBUF, PD = G::PD;
     __shared__ __attribute__((aligned(1024))) char kv_lds[NBUF][2][G::TILE];   // [buffer][K, V]
@@ -697,41 +709,51 @@ __global__ __launch_bounds__(64 * MGeo<D>::NW) void rows_mfma_kernel(RowsParams 
         report(p.err, errbits);
 }
 
-template <int D, int MASK>
+template <int D, int MASK, bool SMALL>
 void launch_kind_m(const RowsParams &p, int kind, int n_qt, hipStream_t st)
 {
     const dim3 grid((unsigned)(n_qt * p.n_split_max * p.n_segments * p.hkv));
-    const dim3 block(64 * MGeo<D>::NW);
+    const dim3 block(64 * MGeo<D, SMALL>::NW);
     switch (kind) {
     case TF_KV_CONTIG:
-        hipLaunchKernelGGL((rows_mfma_kernel<D, TF_KV_CONTIG, MASK>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((rows_mfma_kernel<D, TF_KV_CONTIG, MASK, SMALL>), grid, block, 0, st, p);
         break;
     case TF_KV_PAGED:
-        hipLaunchKernelGGL((rows_mfma_kernel<D, TF_KV_PAGED, MASK>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((rows_mfma_kernel<D, TF_KV_PAGED, MASK, SMALL>), grid, block, 0, st, p);
         break;
     default:
-        hipLaunchKernelGGL((rows_mfma_kernel<D, TF_KV_RING, MASK>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((rows_mfma_kernel<D, TF_KV_RING, MASK, SMALL>), grid, block, 0, st, p);
         break;
     }
 }
 
-template <int D>
+template <int D, bool SMALL = false>
 hipError_t launch_mask_m(const RowsParams &p, int kind, int n_qt, hipStream_t st)
 {
     if (p.mask == TF_MASK_TREE)
-        launch_kind_m<D, TF_MASK_TREE>(p, kind, n_qt, st);
+        launch_kind_m<D, TF_MASK_TREE, SMALL>(p, kind, n_qt, st);
     else if (p.mask == TF_MASK_FULL)
-        launch_kind_m<D, TF_MASK_FULL>(p, kind, n_qt, st);
+        launch_kind_m<D, TF_MASK_FULL, SMALL>(p, kind, n_qt, st);
     else
-        launch_kind_m<D, TF_MASK_CAUSAL>(p, kind, n_qt, st);
+        launch_kind_m<D, TF_MASK_CAUSAL, SMALL>(p, kind, n_qt, st);
     return hipGetLastError();
+}
+
+// The head-dim-256 launch takes the small shape when no segment has more
+// query vectors per kv head than its tile.
+bool small_shape(int head_dim, int64_t max_q)
+{
+    return head_dim == 256 && max_q <= MGeo<256, true>::QB;
 }
 
 }  // namespace
 
-// Query vectors per MFMA workgroup for head dim D.
-int mfma_query_tile(int head_dim)
+// Query vectors per MFMA workgroup for head dim D in a launch whose segments
+// have at most max_q query vectors per kv head.
+int mfma_query_tile(int head_dim, int64_t max_q)
 {
+    if (small_shape(head_dim, max_q))
+        return MGeo<256, true>::QB;
     return head_dim == 256 ? MGeo<256>::QB : (head_dim == 128 ? MGeo<128>::QB : MGeo<64>::QB);
 }
 
@@ -740,7 +762,7 @@ int mfma_query_tile(int head_dim)
 // tile, split, segment, kv head).
 hipError_t launch_rows_mfma(const RowsParams &p, int head_dim, int kind, int max_q, hipStream_t st)
 {
-    const int qb = mfma_query_tile(head_dim);
+    const int qb = mfma_query_tile(head_dim, max_q);
     const int n_qt = (max_q + qb - 1) / qb;
     switch (head_dim) {
     case 64:
@@ -748,6 +770,8 @@ hipError_t launch_rows_mfma(const RowsParams &p, int head_dim, int kind, int max
     case 128:
         return launch_mask_m<128>(p, kind, n_qt, st);
     default:
+        if (small_shape(head_dim, max_q))
+            return launch_mask_m<256, true>(p, kind, n_qt, st);
         return launch_mask_m<256>(p, kind, n_qt, st);
     }
 }

@@ -24,7 +24,8 @@ MASK_SHAPES = [
     ("paged", 64, 8, 4, [2, 1], [33, 500], 32),          # VALU, G 2
     ("ring", 256, 4, 4, [4], [130], 0),                  # VALU, one split
     ("paged", 128, 16, 2, [9, 16, 5], [100, 16, 2000], 64),   # MFMA
-    ("paged", 256, 16, 4, [12], [75], 32),               # MFMA D256, block across tiles and splits
+    ("paged", 256, 16, 4, [12], [75], 32),               # MFMA D256 4-wave blocks, block across tiles and splits
+    ("paged", 256, 16, 4, [24, 3], [400, 90], 64),       # MFMA D256 8-wave blocks (96 vectors)
     ("contig", 64, 8, 1, [7, 3], [300, 45], 96),         # MFMA D64
     ("ring", 128, 16, 2, [64], [4200], 512),             # the 64-row tree limit, wrapped ring
     ("paged", 128, 8, 2, [64, 1], [64, 900], 0),         # 64 rows, no context

@@ -311,17 +311,22 @@ def test_nan_value_poisons_one_lane(gpu):
     assert np.isfinite(got[0:4, 0:4, :77]).all()
 
 
-@pytest.mark.parametrize("d,hq,hkv,rows,dim", [
-    (256, 16, 4, 2, 200),    # 8 query vectors: eight waves split the 16 dim blocks (two each)
-    (256, 16, 4, 7, 37),     # 28 vectors: four waves a block
-    (64, 8, 2, 5, 61),       # D64, 20 vectors: two waves a block
+@pytest.mark.parametrize("d,hq,hkv,rows,dim,other", [
+    # D256 launches of at most 64 query vectors per kv head: 4-wave blocks
+    (256, 16, 4, 2, 200, 0),    # 8 query vectors: four waves split the 16 dim blocks (four each)
+    (256, 16, 4, 7, 37, 0),     # 28 vectors: two waves a block
+    # beside an 80-vector segment the launch takes 8-wave blocks
+    (256, 16, 4, 2, 200, 20),   # eight waves split the dims (two each)
+    (256, 16, 4, 7, 37, 20),    # four waves a block
+    (64, 8, 2, 5, 61, 0),       # D64, 20 vectors: two waves a block
 ])
-def test_nan_value_reaches_its_lane_when_waves_split_dims(gpu, d, hq, hkv, rows, dim):
+def test_nan_value_reaches_its_lane_when_waves_split_dims(gpu, d, hq, hkv, rows, dim, other):
     # a nonfinite value at a visible key poisons exactly its output lane,
     # whichever wave of the block owns that dim (matrix-core kernel)
     keys = 300
-    w = synth.make_workload("nansplit", synth.KIND_PAGED, hq, hkv, d, [rows], [keys], seed=23 + d,
-                            page_size=32, pool_pages=20, split_keys=64)
+    seg_rows = [rows] + ([other] if other else [])
+    w = synth.make_workload("nansplit", synth.KIND_PAGED, hq, hkv, d, seg_rows, [keys] * len(seg_rows),
+                            seed=23 + d + other, page_size=32, pool_pages=40, split_keys=64)
     w.v_logical[0][keys - rows - 5, 0, dim] = synth.BF16_POS_INF       # seen by every row
     w.v_logical[0][keys - 1, 1 % hkv, dim - 1] = synth.BF16_NAN        # seen by the last row only
     w2 = synth.restore(w, synth.KIND_PAGED, seed=4)
@@ -329,7 +334,7 @@ def test_nan_value_reaches_its_lane_when_waves_split_dims(gpu, d, hq, hkv, rows,
     dw.run()
     got, ref = dw.output(), oracle.attn_workload(w2)
     assert_close(got, ref, rel=REL_SMALL, what="nan split dims")
-    g = f32(got)
+    g = f32(got)[:rows]       # the first segment's rows
     group = hq // hkv
     assert np.isnan(g[:, 0:group, dim]).all()
     assert np.isfinite(np.delete(g[:, 0:group, :], dim, axis=2)).all()
@@ -337,6 +342,8 @@ def test_nan_value_reaches_its_lane_when_waves_split_dims(gpu, d, hq, hkv, rows,
     assert np.isnan(g[rows - 1, kv1:kv1 + group, dim - 1]).all()
     if rows > 1 and kv1 != 0:
         assert np.isfinite(g[:rows - 1, kv1:kv1 + group, dim - 1]).all()
+    if other:
+        assert np.isfinite(f32(got)[rows:]).all()
 
 
 def test_nan_in_newest_key_reaches_only_last_row(gpu):
