@@ -197,6 +197,10 @@ SHAPES = [
     # hkv * n_segments a multiple of 8: the matrix-core grid rotates segments by split
     ("paged", 128, 16, 2, [40, 3, 17, 1], [5000, 300, 2100, 64], 512),   # 1 to 5 query tiles
     ("ring", 256, 16, 4, [33, 2], [3000, 1500], 256),
+    # D256 contiguous buffers in both matrix-core shapes (at most 64 query
+    # vectors per kv head: 4-wave blocks; more: 8-wave blocks)
+    ("contig", 256, 16, 4, [3, 12], [900, 260], 128),
+    ("contig", 256, 16, 4, [20, 1], [500, 77], 256),
 ]
 
 
@@ -226,6 +230,7 @@ PAGE_SHAPES = [
     (8, 2, 64, [64], [1500], 512),          # D64 prompt chunk
     (16, 2, 128, [128, 2], [3000, 700], 1024),   # D128 prompt chunk and a short verify
     (16, 4, 256, [1, 24], [1200, 2500], 512),
+    (16, 4, 256, [3, 16], [900, 2100], 512),     # D256 verify (4-wave blocks)
 ]
 
 
