@@ -9,7 +9,8 @@
 // max of keys is order-independent, so the pick does not depend on how the
 // row is cut up.  Phase 1: one workgroup per (row, 8192-logit chunk) reduces
 // its chunk to a key and a flag.  Phase 2: one wave per row reduces the
-// chunks.
+// chunks.  A row of one chunk (vocabularies up to 8192) is finished by
+// phase 1, which then writes the id and flag itself: one launch.
 #include "device.hpp"
 
 namespace tfa {
@@ -33,7 +34,8 @@ __device__ __forceinline__ uint32_t rank16(uint32_t b, uint32_t &nonfinite)
 __global__ __launch_bounds__(kThreads) void argmax_chunks(const uint16_t *logits, int vocab,
                                                           int64_t row_stride, int n_chunks,
                                                           int vec_ok, uint64_t *keys,
-                                                          uint32_t *flags)
+                                                          uint32_t *flags, int32_t *row_ids,
+                                                          uint8_t *row_flags)
 {
     const int chunk = blockIdx.x % n_chunks;
     const int row = blockIdx.x / n_chunks;
@@ -84,6 +86,11 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks(const uint16_t *logits
             nonfinite |= sf[w];
         }
         const uint32_t id = (uint32_t)c0 + (0xFFFFu - (best & 0xFFFFu));
+        if (n_chunks == 1) {
+            row_ids[row] = (int32_t)id;
+            row_flags[row] = nonfinite ? 1 : 0;
+            return;
+        }
         const uint64_t key = ((uint64_t)(best >> 16) << 32) | (uint64_t)(0xFFFFFFFFu - id);
         keys[(int64_t)row * n_chunks + chunk] = key;
         flags[(int64_t)row * n_chunks + chunk] = nonfinite;
@@ -132,7 +139,9 @@ hipError_t launch_argmax(const uint16_t *logits, int n_rows, int vocab, int64_t 
     uint32_t *cflags = reinterpret_cast<uint32_t *>(keys + (int64_t)n_rows * n_chunks);
     const int vec_ok = ((reinterpret_cast<uintptr_t>(logits) & 15u) == 0 && (row_stride & 7) == 0) ? 1 : 0;
     hipLaunchKernelGGL(argmax_chunks, dim3((unsigned)(n_chunks * n_rows)), dim3(kThreads), 0, st,
-                       logits, vocab, row_stride, n_chunks, vec_ok, keys, cflags);
+                       logits, vocab, row_stride, n_chunks, vec_ok, keys, cflags, ids, flags);
+    if (n_chunks == 1)
+        return hipGetLastError();
     hipLaunchKernelGGL(argmax_rows, dim3((unsigned)((n_rows + 3) / 4)), dim3(kThreads), 0, st, n_rows,
                        n_chunks, keys, cflags, ids, flags);
     return hipGetLastError();
