@@ -10,16 +10,22 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "stream_paged_attention_amd", "csrc")
 
 
+_ASM = {}
+
+
 def _asm(src, tmp_path):
-    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    if not os.path.exists(hipcc):
-        pytest.skip("hipcc not available")
-    out = tmp_path / "k.s"
-    subprocess.run([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
-                    "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-                    "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)],
-                   check=True, capture_output=True)
-    return out.read_text().splitlines()
+    """gfx950 assembly of one source file (compiled once per session)."""
+    if src not in _ASM:
+        hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+        if not os.path.exists(hipcc):
+            pytest.skip("hipcc not available")
+        out = tmp_path / (src + ".s")
+        subprocess.run([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+                        "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+                        "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)],
+                       check=True, capture_output=True)
+        _ASM[src] = out.read_text().splitlines()
+    return _ASM[src]
 
 
 def test_m0_is_only_written_for_the_tile_dma(tmp_path):
@@ -41,3 +47,37 @@ def test_no_packed_fp32_arithmetic(tmp_path):
     for src in sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")):
         for ln in _asm(src, tmp_path):
             assert not re.search(r"\bv_pk_(add|mul|fma)_f32\b", ln), (src, ln)
+
+
+def _descriptors(lines):
+    """kernel name -> {field: int} from the .amdhsa_kernel blocks."""
+    out, name = {}, None
+    for ln in lines:
+        ln = ln.strip()
+        if ln.startswith(".amdhsa_kernel "):
+            name = ln.split()[1]
+            out[name] = {}
+        elif ln.startswith(".end_amdhsa_kernel"):
+            name = None
+        elif name and ln.startswith(".amdhsa_"):
+            parts = ln.split()
+            if len(parts) == 2 and parts[1].lstrip("-").isdigit():
+                out[name][parts[0]] = int(parts[1])
+    return out
+
+
+def test_rows_kernels_use_no_scratch_and_the_small_shape_fits_two_a_cu(tmp_path):
+    # no rows kernel spills to scratch; the head-dim-256 shape for small
+    # query tiles keeps registers within two waves a SIMD (<= 256) and its
+    # LDS within half a CU's 160 KB, so two of its 4-wave workgroups share a CU
+    small = 0
+    for src in ("rows_mfma.hip", "rows_valu.hip"):
+        desc = _descriptors(_asm(src, tmp_path))
+        assert desc, src
+        for name, d in desc.items():
+            assert d[".amdhsa_private_segment_fixed_size"] == 0, name
+            if "rows_mfma_kernelILi256" in name and name.endswith("ELb1EEEvNS_10RowsParamsE"):
+                small += 1
+                assert d[".amdhsa_next_free_vgpr"] <= 256, name
+                assert d[".amdhsa_group_segment_fixed_size"] <= 80 * 1024, name
+    assert small == 9   # 3 storage kinds x 3 masks
