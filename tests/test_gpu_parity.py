@@ -3,7 +3,8 @@
 Tolerance: |bf16 output - float64 oracle| <= 2e-3 for the
 five synthetic workloads, NaN positions identical; argmax ids and flags
 bit-exact.  Small hand-shaped cases can produce outputs of magnitude >= 0.5,
-where bf16's own half-ulp (2^-9 |x|) exceeds 2e-3; there the bound is
+where bf16's own rounding exceeds 2e-3: half an ulp of x is between 2^-9 |x|
+(top of a binade) and 2^-8 |x| (bottom of a binade).  There the bound is
 2e-3 + 2^-8 |oracle| (the rounding of the stored result plus the fp32 path).
 """
 import math
@@ -51,29 +52,22 @@ def workloads(gpu):
 
 # --------------------------------------------------------------------------- the five workloads
 
-@pytest.mark.parametrize("name", ["single64", "decode16", "verify8", "ring17"])
+@pytest.mark.parametrize("name", ["single64", "decode16", "verify8", "prompt512", "ring17"])
 def test_workload_matches_oracle(workloads, name):
+    # every output element of the workload against the float64 oracle (the
+    # prompt chunk's 512 x 16 x 256 outputs take the oracle ~10 s on 16 cores)
     w, dw = workloads(name)
     print(f"{name}: {synth.WORKLOAD_TITLES[name]}", flush=True)
     assert dw.check_table() == binding.TF_OK
+    dw.out.fill_(0x7FA5)          # a NaN pattern no kernel writes: every element must be overwritten
     dw.run()
     got = dw.output()
+    assert not np.any(got == 0x7FA5), f"{name}: output elements left unwritten"
     ref = oracle.attn_workload(w)
+    assert ref.shape == got.shape
     err = assert_close(got, ref, what=name)
     assert dw.error_word() == 0
-    print(f"{name}: max |err| = {err:.3e}")
-
-
-def test_prompt512_sampled_rows_match_oracle(workloads):
-    w, dw = workloads("prompt512")
-    dw.run()
-    got = dw.output()
-    rng = np.random.Generator(np.random.PCG64(44))
-    rows = sorted(set([0, 1, 31, 32, 255, 256, 510, 511] + rng.choice(512, 16, replace=False).tolist()))
-    ref = oracle.attn_workload(w, rows=rows)
-    err = assert_close(got[rows], ref, what="prompt512 sampled rows")
-    assert dw.error_word() == 0
-    print(f"prompt512: {len(rows)} sampled rows, max |err| = {err:.3e}")
+    print(f"{name}: {got.size} outputs, max |err| = {err:.3e}")
 
 
 @pytest.mark.parametrize("name", ["single64", "verify8", "ring17"])
@@ -110,15 +104,21 @@ def test_rotated_grid_batched_equals_per_segment(gpu):
     assert dw.error_word() == 0
 
 
-def test_repeats_are_byte_identical(workloads):
-    w, dw = workloads("decode16")
-    outs = []
-    for _ in range(5):
-        dw.out.zero_()
+@pytest.mark.parametrize("name", ["decode16", "verify8", "prompt512", "ring17"])
+def test_repeats_are_byte_identical(workloads, name):
+    # five runs give the same bytes: the decode kernel (decode16) and the
+    # matrix-core kernel with its hand-counted DMA waits (verify8, prompt512,
+    # ring17); the first run's bytes are compared with each later one at once
+    w, dw = workloads(name)
+    first = None
+    for i in range(5):
+        dw.out.fill_(0x7FA5)
         dw.run()
-        outs.append(dw.output().copy())
-    for o in outs[1:]:
-        assert np.array_equal(o, outs[0])
+        o = dw.output().copy()
+        if first is None:
+            first = o
+        else:
+            assert np.array_equal(o, first), f"{name}: run {i} differs from run 0"
 
 
 # --------------------------------------------------------------------------- storage equalities
