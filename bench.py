@@ -9,8 +9,13 @@ Default workload: 16 one-row decode streams, 32 query / 8 kv heads, head dim
 Inputs are resident in HBM before timing starts.  The K/V pool is kept in
 ``--copies`` copies (each with its own segment table) and the steps rotate
 over them, so that K/V is read from HBM and not from the 256 MB Infinity
-Cache.  Printed: one JSON line (metric, value = KV-read GB/s of the whole
-step, roofline of the rows kernel, the CPU oracle's rate on the host cores).
+Cache.  Printed: one JSON line: metric, value = KV-read GB/s of the whole
+step over exactly --steps steps, the step's median / p10 / p90 over
+--dist-steps steps timed one by one, the roofline of the rows kernel, a
+measured device-copy ceiling, a side table with the other four workloads
+(attention step and argmax, each timed step by step, with its roofline
+fraction), and the CPU oracle's rate on every host core and on one core,
+with the CPU model.
 """
 from __future__ import annotations
 
@@ -59,31 +64,55 @@ def traffic_entry(name: str):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(w, budget_s: float, threads: int):
+    """Run the oracle over the whole workload (or a row sample of the prompt
+    chunk) repeatedly for about budget_s; rates from the median repetition."""
     from oracle import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
     rows = None
     if w.name == "prompt512":      # bounded sample: a few rows of the prompt chunk
         rows = [0, 128, 256, 384, 511]
-    reps, used = 0, threads
-    t0 = time.perf_counter()
+    times, used = [], threads
+    t_end = time.perf_counter() + budget_s
     while True:
+        t0 = time.perf_counter()
         _, used = oracle.attn_workload(w, rows=rows, threads=threads, return_threads=True)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() >= t_end and len(times) >= 3:
             break
+    med = sorted(times)[len(times) // 2]
     if rows is None:
         nbytes, nrows = kv_bytes(w), w.total_rows
-        sample = f"whole workload x{reps} ({el:.1f} s)"
+        sample = f"whole workload, median of {len(times)} runs ({sum(times):.1f} s)"
     else:
         seg = w.segments[0]
         nbytes = sum(seg.key_count - seg.n_rows + r + 1 for r in rows) * w.n_kv_heads * w.head_dim * 4
         nrows = len(rows)
-        sample = f"{len(rows)} of {w.total_rows} rows x{reps} ({el:.1f} s)"
-    return {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": int(used),
-            "kind": "oracle", "sample": sample,
-            "rows_per_s": round(nrows * reps / el, 2)}
+        sample = f"{len(rows)} of {w.total_rows} rows, median of {len(times)} runs ({sum(times):.1f} s)"
+    return {"value": round(nbytes / med / 1e9, 4), "unit": "GB/s", "cores": int(used),
+            "kind": "oracle", "sample": sample, "rows_per_s": round(nrows / med, 2),
+            "median_s": round(med, 5)}
+
+
+def cpu_baseline(w, budget_s: float):
+    """The float64 oracle on every host core, and again on one core."""
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    out = _oracle_rate(w, budget_s, threads)
+    one = _oracle_rate(w, max(3.0, budget_s / 3), 1)
+    out["cpu_model"] = cpu_model()
+    out["nproc"] = os.cpu_count()
+    out["one_core"] = {k: one[k] for k in ("value", "cores", "sample", "rows_per_s", "median_s")}
+    return out
 
 
 def bench_kv_put(args, w, dw, copies, stream) -> int:
@@ -194,6 +223,144 @@ def bench_state(args) -> int:
     return 0
 
 
+def percentiles(xs):
+    """(median, p10, p90) of a list of floats."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return float(np.median(a)), float(np.percentile(a, 10)), float(np.percentile(a, 90))
+
+
+class AttnStep:
+    """One workload resident on the device: its K/V copies, tables, logits and
+    the step (tf_attn_rows, tf_attn_merge when split, tf_argmax when the
+    workload has logits) on the current stream."""
+
+    def __init__(self, name: str, dev, copies: int = 0):
+        import torch
+        from stream_paged_attention_amd import binding, launch, synth
+        self.binding = binding
+        self.name = name
+        self.w = w = synth.make_synthetic(name)
+        self.copies = copies or max(1, min(8, -(-(2 * 256 * 2 ** 20) // max(1, kv_bytes(w)))))
+        self.dw = launch.DeviceWorkload(w, dev, copies=self.copies)
+        self.stream = torch.cuda.current_stream(dev)
+        self.st = self.stream.cuda_stream
+        self.argl = [self.dw.args(c) for c in range(self.copies)]
+        self.split = self.dw.split_keys > 0
+        self.logits = None
+        if w.logits is not None:
+            self.logits = launch._dev(w.logits, dev)
+            self.nrows, self.vocab = w.logits.shape
+            self.ids = torch.empty(self.nrows, dtype=torch.int32, device=dev)
+            self.flags = torch.empty(self.nrows, dtype=torch.uint8, device=dev)
+            self.wsb = binding.tf_argmax_workspace_bytes(self.nrows, self.vocab)
+            self.ws = torch.empty(self.wsb // 8 + 1, dtype=torch.int64, device=dev)
+
+    def attn(self, i: int) -> int:
+        a = self.argl[i % self.copies]
+        rc = self.binding.tf_attn_rows(a, self.st)
+        if self.split:
+            rc |= self.binding.tf_attn_merge(a, self.st)
+        return rc
+
+    def rows_only(self, i: int) -> int:
+        return self.binding.tf_attn_rows(self.argl[i % self.copies], self.st)
+
+    def argmax(self, i: int) -> int:
+        return self.binding.tf_argmax(self.logits.data_ptr(), self.nrows, self.vocab, self.vocab,
+                                      self.ids.data_ptr(), self.flags.data_ptr(), self.ws.data_ptr(),
+                                      self.wsb, self.st)
+
+    def full(self, i: int) -> int:
+        rc = self.attn(i)
+        if self.logits is not None:
+            rc |= self.argmax(i)
+        return rc
+
+    def time_total(self, fn, steps: int, warmup: int) -> float:
+        """Mean microseconds per call over exactly `steps` calls between one event pair."""
+        import torch
+        for i in range(warmup):
+            assert fn(i) == 0
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        for i in range(steps):
+            fn(i)
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / steps
+
+    def time_each(self, fn, steps: int, warmup: int):
+        """Per-call microseconds: an event before every call and after the last."""
+        import torch
+        for i in range(warmup):
+            assert fn(i) == 0
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        for i in range(steps):
+            ev[i].record(self.stream)
+            fn(i)
+        ev[steps].record(self.stream)
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]
+
+    def error_word(self) -> int:
+        return self.dw.error_word()
+
+
+def copy_ceiling_gbps(dev, mib: int = 1024, reps: int = 10) -> float:
+    """Bytes read plus bytes written per second by a plain device-to-device copy."""
+    import torch
+    x = torch.ones(mib << 20, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        y.copy_(x)
+    b.record()
+    torch.cuda.synchronize()
+    s = a.elapsed_time(b) * 1e-3 / reps
+    del x, y
+    torch.cuda.empty_cache()
+    return 2 * (mib << 20) / s / 1e9
+
+
+def workload_entry(ws: "AttnStep", n_dist: int) -> dict:
+    """Per-step distribution and roofline fraction of one workload's attention
+    (and argmax), for the side table of the bench line."""
+    w = ws.w
+    kvb, flops = kv_bytes(w), attn_flops(w)
+    med, p10, p90 = percentiles(ws.time_each(ws.attn, n_dist, 10))
+    rows_us = ws.time_total(ws.rows_only, n_dist, 10)
+    e = {"attn_us_median": round(med, 3), "attn_us_p10": round(p10, 3), "attn_us_p90": round(p90, 3),
+         "rows_kernel_us": round(rows_us, 3), "kv_bytes": kvb, "attn_flops": flops,
+         "value_gbps": round(kvb / (med * 1e-6) / 1e9, 2),
+         "rows_per_s": round(w.total_rows / (med * 1e-6), 1),
+         "hbm_frac": round(kvb / (rows_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+         "mfma_frac": round(flops / (rows_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if ws.logits is not None:
+        am, a10, a90 = percentiles(ws.time_each(ws.argmax, n_dist, 10))
+        lb = ws.nrows * ws.vocab * 2
+        e.update({"argmax_us_median": round(am, 3), "argmax_us_p10": round(a10, 3),
+                  "argmax_us_p90": round(a90, 3), "argmax_logit_bytes": lb,
+                  "argmax_hbm_frac": round(lb / (am * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                  "step_us_mean": round(ws.time_total(ws.full, n_dist, 10), 3)})
+    if w.name == "prompt512":
+        e["bound"] = "mfma"
+    elif w.name == "single64":
+        e["bound"] = "latency"
+    else:
+        e["bound"] = "hbm"
+    assert ws.error_word() == 0
+    return e
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,8 +370,12 @@ def main() -> int:
                     choices=["single64", "decode16", "verify8", "prompt512", "ring17"],
                     help="synthetic workload (decode16: the 16-stream decode the metric is quoted on)")
     ap.add_argument("--copies", type=int, default=0, help="K/V copies rotated (0 = auto)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-side", action="store_true",
+                    help="skip the other workloads' side table and the copy ceiling")
+    ap.add_argument("--dist-steps", type=int, default=200,
+                    help="steps timed one by one for the median and p10/p90 (at least 100)")
     ap.add_argument("--kernel-only", action="store_true",
                     help="time only tf_attn_rows launches (for profiler runs)")
     ap.add_argument("--op", choices=["attn", "kv_put", "state"], default="attn",
@@ -218,9 +389,10 @@ def main() -> int:
               "(the path shards by stream or by kv head with no exchange between GPUs)",
               file=sys.stderr)
         return 2
+    args.dist_steps = max(100, args.dist_steps)
 
     import torch
-    from stream_paged_attention_amd import binding, launch, synth
+    from stream_paged_attention_amd import binding, synth
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -237,60 +409,34 @@ def main() -> int:
     binding.load()
     if args.op == "state":
         return bench_state(args)
-    w = synth.make_synthetic(args.workload)
+    ws = AttnStep(args.workload, dev, args.copies)
+    w, dw, copies = ws.w, ws.dw, ws.copies
     pool_bytes = (w.pool_k.nbytes * 2 if w.pool_k is not None
                   else sum(x.nbytes for x in w.store_k) * 2)
-    copies = args.copies or max(1, min(8, -(-(2 * 256 * 2 ** 20) // max(1, kv_bytes(w)))))
-    dw = launch.DeviceWorkload(w, dev, copies=copies)
-    stream = torch.cuda.current_stream(dev)
-    st = stream.cuda_stream
-    argl = [dw.args(c) for c in range(copies)]
-    logits = ids = flags = ws = None
-    if w.logits is not None and not args.kernel_only:
-        logits = launch._dev(w.logits, dev)
-        nrows, vocab = w.logits.shape
-        ids = torch.empty(nrows, dtype=torch.int32, device=dev)
-        flags = torch.empty(nrows, dtype=torch.uint8, device=dev)
-        wsb = binding.tf_argmax_workspace_bytes(nrows, vocab)
-        ws = torch.empty(wsb // 8 + 1, dtype=torch.int64, device=dev)
-    split = dw.split_keys > 0
     if args.op == "kv_put":
-        return bench_kv_put(args, w, dw, copies, stream)
+        return bench_kv_put(args, w, dw, copies, ws.stream)
+    step = ws.rows_only if args.kernel_only else ws.full
 
-    def step(i):
-        a = argl[i % copies]
-        rc = binding.tf_attn_rows(a, st)
-        if split and not args.kernel_only:
-            rc |= binding.tf_attn_merge(a, st)
-        if logits is not None:
-            rc |= binding.tf_argmax(logits.data_ptr(), nrows, vocab, vocab, ids.data_ptr(),
-                                    flags.data_ptr(), ws.data_ptr(), wsb, st)
-        return rc
-
+    # the timed region: exactly K steps between two events on the launch stream
     for i in range(args.warmup):
         assert step(i) == 0
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    start.record(stream)
+    start.record(ws.stream)
     for i in range(args.steps):
         step(i)
-    end.record(stream)
+    end.record(ws.stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
-    # the rows kernel alone: the same launches back to back between one event
-    # pair on the launch stream (average launch duration, gaps included)
-    n_rows_runs = min(args.steps, 1000)
-    start.record(stream)
-    for i in range(n_rows_runs):
-        binding.tf_attn_rows(argl[i % copies], st)
-    end.record(stream)
-    torch.cuda.synchronize()
-    rows_avg_ms = start.elapsed_time(end) / n_rows_runs
-    assert dw.error_word() == 0
+    ms_step = start.elapsed_time(end) / args.steps
+    # the same step timed one by one (an event before each): median, p10, p90
+    s_med, s_p10, s_p90 = percentiles(ws.time_each(step, args.dist_steps, 10))
+    # the rows kernel alone: back-to-back launches between one event pair on
+    # the launch stream (average launch duration, gaps included)
+    rows_avg_ms = ws.time_total(ws.rows_only, min(args.steps, 1000), 10) * 1e-3
+    assert ws.error_word() == 0
 
     from stream_paged_attention_amd.profsum import kernel_hash as kernel_hash_now
     kvb = kv_bytes(w)
@@ -329,6 +475,8 @@ def main() -> int:
             "accumulate": "fp32", "kv_copies_rotated": copies, "pool_bytes_per_copy": pool_bytes,
             "rows_per_s": round(w.total_rows / (ms_step * 1e-3), 1),
             "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+            "step_us_median": round(s_med, 3), "step_us_p10": round(s_p10, 3),
+            "step_us_p90": round(s_p90, 3), "dist_steps": args.dist_steps,
             "rows_kernel_us": round(rows_avg_ms * 1e3, 3),
             "wall_s": round(wall, 3),
             "kernel_hash": kernel_hash_now(),
@@ -338,6 +486,17 @@ def main() -> int:
                      "kernel": kernel,
                      "hbm_gbps_rows_kernel": round(achieved_hbm, 2)},
     }
+    if not args.no_side and not args.kernel_only:
+        out["copy_ceiling_gbps"] = round(copy_ceiling_gbps(dev), 1)
+        side = {}
+        for name in synth.WORKLOADS:
+            if name == args.workload:
+                continue
+            other = AttnStep(name, dev)
+            side[name] = workload_entry(other, args.dist_steps)
+            del other
+            torch.cuda.empty_cache()
+        out["workloads"] = side
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

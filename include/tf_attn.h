@@ -100,7 +100,12 @@ enum {
                               n_rows > 64 under TF_MASK_TREE                                   */
     TF_ERR_BAD_RING = 8,   /* ring first outside [0, capacity)                                   */
     TF_ERR_PARTIALS = 16,  /* the segment's partial records fall outside the workspace           */
-    TF_ERR_BAD_LAYER = 32  /* tf_state_*: a layer's pointer is null or not 16-byte aligned       */
+    TF_ERR_BAD_LAYER = 32, /* tf_state_*: a layer's pointer is null or not 16-byte aligned       */
+    TF_ERR_HINTS = 64,     /* n_rows > max_rows or key_count > max_keys: the launch's grid does not
+                              cover the segment; the rows it covers are written as NaN, the rest
+                              of the segment's rows and splits are not written                   */
+    TF_ERR_STORAGE = 128   /* CONTIG / RING: one kv head's run of the buffer, capacity * head_dim
+                              * 2 bytes, is 4 GiB or more (beyond the kernels' 32-bit offsets)  */
 };
 
 /*
@@ -173,7 +178,13 @@ typedef struct tf_attn_args {
 } tf_attn_args;
 
 /*
- * tf_attn_rows: attention of every segment's rows over its own keys.
+ * tf_attn_rows: attention of every segment's rows over its own keys
+ * (TensorFold PR #1503, the shared-rounds commit: one launch per layer serves
+ * every stream's rows from the segment table, partials held apart per
+ * stream; PR #1653, the paged decode part kernel and the paged prompt rows
+ * read through the page table with the page id looked up once per tile;
+ * PR #1562, one rows kernel for all streams of a round, bit-equal to a
+ * launch per stream, ring slots read with the next group in flight).
  * With split_keys > 0 writes one partial record per (row, head, split) of
  * every segment; with split_keys == 0 writes out.  Each (row, head)'s
  * result depends only on its own segment: a batched launch is bit-equal to
@@ -298,7 +309,8 @@ size_t tf_argmax_workspace_bytes(int32_t n_rows, int32_t vocab);
 /*
  * tf_plan_partials (host): assign each segment's partial_offset in the
  * host table (segments laid out in order) and return the workspace size in
- * bytes for split_keys > 0.  Reads n_rows and key_count of each host
+ * bytes for split_keys > 0 (TensorFold PR #1503, the shared-rounds commit:
+ * the caller owns the scratch the partials live in, one range per stream).  Reads n_rows and key_count of each host
  * segment.  Returns TF_E_INVALID on bad counts, TF_E_UNSUPPORTED on a bad
  * split_keys or head_dim.
  */
@@ -308,11 +320,15 @@ int tf_plan_partials(tf_segment *host_segs, int32_t n_segments, int32_t n_q_head
 /*
  * tf_check_segments (host): the kernels' per-segment checks on a host copy
  * of the table, plus the ones only the host can do (rows of different
- * segments must not overlap; max_rows / max_keys must bound the table; the
- * pages pointer of a PAGED segment must be non-null).  Returns TF_OK,
- * TF_E_PAST_PAGES (a segment holds more keys than its storage),
- * TF_E_WORKSPACE (partial records outside the workspace) or TF_E_INVALID.
- * Page ids live in device memory and are checked by the kernels only.
+ * segments must not overlap; the pages pointer of a PAGED segment must be
+ * non-null).  max_rows / max_keys must bound the table (the kernels flag a
+ * segment past them with TF_ERR_HINTS).  Returns TF_OK, TF_E_PAST_PAGES (a
+ * segment holds more keys than its storage), TF_E_WORKSPACE (partial records
+ * outside the workspace), TF_E_UNSUPPORTED (a CONTIG / RING kv-head run of 4
+ * GiB or more, TF_ERR_STORAGE on the device) or TF_E_INVALID.  Page ids live
+ * in device memory and are checked by the kernels only.  The checks follow
+ * TensorFold PR #1503 (the pool-leasing commit: a slot's rows are refused past
+ * its pages) and the table fields of its shared-rounds commit.
  */
 int tf_check_segments(const tf_attn_args *a, const tf_segment *host_segs);
 

@@ -32,6 +32,8 @@ TF_ERR_BAD_ROWS = 4
 TF_ERR_BAD_RING = 8
 TF_ERR_PARTIALS = 16
 TF_ERR_BAD_LAYER = 32
+TF_ERR_HINTS = 64
+TF_ERR_STORAGE = 128
 
 EXPORTS = ("tf_attn_rows", "tf_attn_merge", "tf_argmax", "tf_argmax_workspace_bytes",
            "tf_kv_put", "tf_state_save", "tf_state_restore", "tf_plan_partials",

@@ -119,6 +119,8 @@ tfa::RowsParams make_params(const tf_attn_args *a)
     p.pool_pages = a->kind == TF_KV_PAGED ? a->pool_pages : 0;
     p.split_keys = a->split_keys;
     p.n_split_max = n_splits_of(a->max_keys, a->split_keys);
+    p.max_rows = a->max_rows;
+    p.max_keys = a->max_keys;
     p.c_log2 = (float)((double)a->scale * 1.4426950408889634073599);
     p.mfma_min_q = tfa::kMfmaMinQ;
     p.mask = a->mask;
@@ -187,7 +189,7 @@ int tf_check_segments(const tf_attn_args *a, const tf_segment *host_segs)
         a->split_keys > 0 ? (int64_t)a->partials_bytes / record_bytes(a->head_dim) : 0;
     std::vector<std::pair<int64_t, int64_t>> spans;
     spans.reserve((size_t)a->n_segments);
-    int past = 0, workspace = 0;
+    int past = 0, workspace = 0, storage = 0;
     for (int i = 0; i < a->n_segments; ++i) {
         const tf_segment &s = host_segs[i];
         if (s.k == nullptr || s.v == nullptr || !aligned16(s.k) || !aligned16(s.v))
@@ -211,6 +213,9 @@ int tf_check_segments(const tf_attn_args *a, const tf_segment *host_segs)
                 return TF_E_INVALID;
             if (a->kind == TF_KV_CONTIG && s.first != 0)
                 return TF_E_INVALID;
+            // one kv head's run must stay within the kernels' 32-bit offsets
+            if ((int64_t)s.capacity * a->head_dim * 2 > 0xFFFFFFFFll)
+                storage = 1;
         }
         if (a->split_keys > 0) {
             const int64_t need = (int64_t)s.n_rows * a->n_q_heads * n_splits_of(s.key_count, a->split_keys);
@@ -223,6 +228,8 @@ int tf_check_segments(const tf_attn_args *a, const tf_segment *host_segs)
     for (size_t i = 1; i < spans.size(); ++i)
         if (spans[i].first < spans[i - 1].second)
             return TF_E_INVALID;   // two segments write the same output rows
+    if (storage)
+        return TF_E_UNSUPPORTED;
     if (past)
         return TF_E_PAST_PAGES;
     if (workspace)

@@ -32,6 +32,8 @@ struct RowsParams {
     int pool_pages;
     int split_keys;        // 0 = one split per (row, head), written straight to out
     int n_split_max;       // grid extent per segment
+    int max_rows;          // the launch's hints: the grid covers n_rows <= max_rows and
+    int max_keys;          // key_count <= max_keys (a segment past them is an error)
     float c_log2;          // scale * log2(e): scores are kept in base-2 units
     int mfma_min_q;        // segments with more query vectors per kv head than this
                            // (n_rows * group) take the matrix-core kernel
@@ -113,6 +115,16 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
 {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Two floats to a packed bf16 pair (low half a), round to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
+{
+    bf16x2_t v;
+    v.x = (__bf16)a;
+    v.y = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Exact widening of the low / high bf16 of a packed pair.
@@ -200,6 +212,35 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Largest kv-head run of a CONTIG / RING buffer, in bytes, that the kernels'
+// 32-bit offsets address.
+constexpr int64_t kMaxHeadRunBytes = 0xFFFFFFFFll;
+
+// Per-segment checks shared by the rows kernels: the launch's hints and the
+// storage kinds' limits.  Returns TF_ERR_* bits (0 = fine).
+template <int KIND>
+__device__ __forceinline__ int segment_errors(const RowsParams &p, const tf_segment &sd, int head_dim)
+{
+    int e = 0;
+    if (sd.n_rows > p.max_rows || sd.key_count > p.max_keys)
+        e |= TF_ERR_HINTS;
+    if constexpr (KIND == TF_KV_PAGED) {
+        if (sd.pages == nullptr || sd.capacity < 0 ||
+            (int64_t)sd.key_count > ((int64_t)sd.capacity << p.page_shift))
+            e |= TF_ERR_PAST_PAGES;
+    } else {
+        if (sd.key_count > sd.capacity)
+            e |= TF_ERR_PAST_PAGES;
+        if ((int64_t)sd.capacity * head_dim * 2 > kMaxHeadRunBytes)
+            e |= TF_ERR_STORAGE;
+    }
+    if constexpr (KIND == TF_KV_RING) {
+        if (sd.first < 0 || sd.first >= sd.capacity)
+            e |= TF_ERR_BAD_RING;
+    }
+    return e;
 }
 
 __device__ __forceinline__ void report(int32_t *err, int bits)

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kPutThreads) void kv_put_kernel(PutParams p, int ma
             report(p.err, TF_ERR_BAD_ROWS);
         return;
     }
-    int bad = 0;
+    int bad = n_rows > max_rows ? TF_ERR_HINTS : 0;   // rows past the grid: skip the segment
     if constexpr (KIND == TF_KV_PAGED) {
         if (sd.pages == nullptr || capacity < 0 || (int64_t)kc > ((int64_t)capacity << p.page_shift))
             bad |= TF_ERR_PAST_PAGES;

@@ -31,7 +31,11 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(RowsParams p, int ma
         return;   // reported by tf_attn_rows; no row can be addressed safely
     const int n_splits = (kc + p.split_keys - 1) / p.split_keys;
     const int64_t first = (int64_t)sd.partial_offset + ((int64_t)r * p.hq + h) * n_splits;
-    const bool parts_ok = sd.partial_offset >= 0 &&
+    // past the hints the rows kernels did not write every record: NaN
+    const bool hints_ok = n_rows <= max_rows && kc <= p.max_keys;
+    if (!hints_ok && r == 0 && h == 0 && lane == 0)
+        report(p.err, TF_ERR_HINTS);
+    const bool parts_ok = hints_ok && sd.partial_offset >= 0 &&
                           (int64_t)sd.partial_offset + (int64_t)n_rows * p.hq * n_splits <= p.max_records;
     uint16_t *dst = p.out + ((size_t)(row_offset + r) * p.hq + h) * D;
     merge_one<D>(p.partials + (parts_ok ? first : 0) * (D + 4), n_splits, parts_ok, dst, lane);

@@ -87,16 +87,6 @@ struct IntC {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t x) { return __builtin_bit_cast(bf16x8_t, x); }
 
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
-{
-    // v_cvt_pk_bf16_f32: round to nearest even
-    typedef __bf16 bf16x2_t2 __attribute__((ext_vector_type(2)));
-    bf16x2_t2 v;
-    v.x = (__bf16)a;
-    v.y = (__bf16)b;
-    return __builtin_bit_cast(uint32_t, v);
-}
-
 // Byte offset of 16-byte unit `c` of key row `key` in an LDS tile.
 template <int D>
 __device__ __forceinline__ uint32_t unit_off(int key, int c)
@@ -200,18 +190,7 @@ __attribute__((amdgpu_waves_per_eu(SMALL ? 2 : 1))) void rows_mfma_kernel(RowsPa
     }
     if (qt * QB >= nq)
         return;
-    int errbits = 0;
-    if constexpr (KIND == TF_KV_PAGED) {
-        if (pages == nullptr || capacity < 0 || (int64_t)kc > ((int64_t)capacity << p.page_shift))
-            errbits |= TF_ERR_PAST_PAGES;
-    } else {
-        if (kc > capacity)
-            errbits |= TF_ERR_PAST_PAGES;
-    }
-    if constexpr (KIND == TF_KV_RING) {
-        if (first < 0 || first >= capacity)
-            errbits |= TF_ERR_BAD_RING;
-    }
+    int errbits = segment_errors<KIND>(p, sd, D);
     const int n_splits = p.split_keys > 0 ? (kc + p.split_keys - 1) / p.split_keys : 1;
     if (t >= n_splits)
         return;

@@ -40,22 +40,32 @@ constexpr float kLazy = 8.0f;   // log2 of the largest weight a stale reference 
 
 // Shape of one pass: LPK lanes per key, DPL dims per lane, NS wave steps of
 // KPS keys per tile, CH tiles in flight per wave.  8 lanes per key where the
-// accumulators fit (3 DPP steps per 8 keys), 16 otherwise.
+// accumulators fit (3 DPP steps per 8 keys: D 64 and 128), 16 at D 256.
 template <int D, int QT>
 struct Geo {
-    static constexpr int LPK = (D == 256 || (D == 128 && QT > 4)) ? 16 : 8;
+    static constexpr int LPK = D == 256 ? 16 : 8;
     static constexpr int KPS = 64 / LPK;              // keys per wave step
     static constexpr int DPL = D / LPK;               // dims per lane
     static constexpr int W = DPL / 2;                 // packed bf16 pairs per lane per key
     static constexpr int NS = (DPL <= 8) ? 2 : 1;     // wave steps per tile
     static constexpr int TK = NS * KPS;               // keys per tile
-    static constexpr int CH = 2;                      // tiles in flight per wave
+    // Key pairs (8 lanes a key: D 64 and 128): the key groups 2i and 2i+1 of
+    // a 16-lane row hold adjacent keys; each lane of the pair loads the same
+    // half of both keys' values and accumulates that half of the output over
+    // both keys with one v_dot2_f32_bf16 per dim pair, the weights rounded
+    // to bf16 (fp32 sums).  The output accumulators halve, which pays for
+    // more tiles in flight.
+    static constexpr bool PAIR = LPK == 8;
+    static constexpr int OPL = PAIR ? DPL / 2 : DPL;  // output dims accumulated per lane
+    static constexpr int WV = PAIR ? W / 2 : W;       // value registers per key and step
+    static constexpr int CH = PAIR ? 3 : 2;           // tiles in flight per wave
     // Partial sums parked in LDS per wave and query vector: one per 16-lane
     // row (R = 4), or per row pair / per wave (R = 2, 1) where 4 would not
     // fit in 32 KB per workgroup.
     static constexpr int R4_BYTES = kWaves * QT * 4 * D * 4;
     static constexpr int R = R4_BYTES <= 32768 ? 4 : (R4_BYTES / 2 <= 32768 ? 2 : 1);
     static_assert(DPL == 4 || DPL % 8 == 0, "lane slice must be 8 bytes or whole 16-byte chunks");
+    static_assert(!PAIR || (R == 4 && OPL % 4 == 0), "pair mode keeps one output row per 16 lanes");
 };
 
 // Dimension of element e (0 .. DPL-1) of lane sub-index sl: 16-byte chunk c
@@ -69,6 +79,49 @@ __device__ __forceinline__ int lane_dim(int sl, int e)
         return sl * 4 + e;
     else
         return (e >> 3) * (8 * G::LPK) + sl * 8 + (e & 7);
+}
+
+// Dimension of output element i (0 .. OPL-1) of a lane in the pair mode:
+// the even lane of a pair keeps the first half of its slice (16-byte chunk
+// 0 at D 128, the first 8 bytes at D 64), the odd lane the second half.
+template <int D, int QT>
+__device__ __forceinline__ int pair_dim(int sl, int odd, int i)
+{
+    using G = Geo<D, QT>;
+    if constexpr (G::DPL == 8)
+        return sl * 8 + odd * 4 + i;
+    else
+        return odd * (8 * G::LPK) + sl * 8 + i;
+}
+
+// Byte offset, within a key row, of the half slice a pair-mode lane keeps.
+template <int D, int QT>
+__device__ __forceinline__ uint32_t pair_lane_bytes(int sl, int odd)
+{
+    using G = Geo<D, QT>;
+    if constexpr (G::DPL == 8)
+        return (uint32_t)(sl * 16 + odd * 8);
+    else
+        return (uint32_t)(odd * 16 * G::LPK + sl * 16);
+}
+
+// Load the kept half slice (WV registers) of one value row.
+template <int D, int QT>
+__device__ __forceinline__ void load_half(uint32_t *r, const char *base, uint32_t off)
+{
+    using G = Geo<D, QT>;
+    if constexpr (G::WV == 2) {
+        const u32x2_t x = load_stream<u32x2_t>(base + off);
+        r[0] = x.x;
+        r[1] = x.y;
+    } else {
+        static_assert(G::WV == 4, "a half slice is 8 or 16 bytes");
+        const u32x4_t x = load_stream<u32x4_t>(base + off);
+        r[0] = x.x;
+        r[1] = x.y;
+        r[2] = x.z;
+        r[3] = x.w;
+    }
 }
 
 // Load the lane's slice of one key row: base is uniform across the wave
@@ -112,6 +165,26 @@ __device__ __forceinline__ void store_f32(float *dst, const float *o, int sl)
     }
 }
 
+// acc + a.lo * b.lo + a.hi * b.hi in the three-address form (VOP3), so that
+// a long-lived accumulator need not share its register with the result
+// (the two-address v_dot2c form made the compiler copy the accumulators)
+__device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float acc)
+{
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(acc));
+    return r;
+}
+
+template <int D, int QT>
+__device__ __forceinline__ void store_pair_f32(float *dst, const float *o, int sl, int odd)
+{
+    using G = Geo<D, QT>;
+    float *p = dst + pair_dim<D, QT>(sl, odd, 0);
+#pragma unroll
+    for (int i = 0; i < G::OPL; i += 4)
+        *reinterpret_cast<float4 *>(p + i) = make_float4(o[i], o[i + 1], o[i + 2], o[i + 3]);
+}
+
 // Sum over the LPK lanes of a key group (DPP: quad swaps, half-row mirror,
 // row mirror); every lane of the group receives the sum.
 template <int LPK>
@@ -148,21 +221,27 @@ struct Addr {
     int ring0;       // RING: slot of logical key 0
     int cap;
     uint32_t lane_b; // byte offset of the lane's slice within a row
+    int delta;       // pair mode: the partner key is this lane's key + delta (+-1)
+    uint32_t lane_v; // pair mode: byte offset of the kept half slice within a row
 
-    __device__ __forceinline__ uint32_t at(int j) const
+    // row of the lane's key (dk = 0) or its partner's (dk = delta) at wave
+    // step j, plus the byte offset b within the row
+    __device__ __forceinline__ uint32_t row_at(int j, int dk, uint32_t b) const
     {
         constexpr int KPS = Geo<D, QT>::KPS;
         constexpr uint32_t ROW = D * 2;
         if constexpr (KIND == TF_KV_PAGED) {
-            return off0 + (uint32_t)(KPS * j) * ROW;
+            // pairs (2i, 2i+1) never straddle a page
+            return off0 + (uint32_t)(KPS * j + dk) * ROW + b;
         } else if constexpr (KIND == TF_KV_CONTIG) {
-            return (uint32_t)min(first + KPS * j, last) * ROW + lane_b;
+            return (uint32_t)min(first + dk + KPS * j, last) * ROW + b;
         } else {
-            int slot = ring0 + min(first + KPS * j, last);
+            int slot = ring0 + min(first + dk + KPS * j, last);
             slot -= (slot >= cap) ? cap : 0;
-            return (uint32_t)slot * ROW + lane_b;
+            return (uint32_t)slot * ROW + b;
         }
     }
+    __device__ __forceinline__ uint32_t at(int j) const { return row_at(j, 0, lane_b); }
 };
 
 __device__ __forceinline__ float uniform(float x)
@@ -179,7 +258,7 @@ struct State {
     float thr[QT];  // m + 8 / c: a score above it raises the reference
     float lo[QT];   // min of the counted scores (-inf flags a -inf score)
     float l[QT];
-    float o[QT][Geo<D, QT>::DPL];
+    float o[QT][Geo<D, QT>::OPL];
 };
 
 // max / min as a single v_max_f32 / v_min_f32: the compiler's versions for
@@ -220,11 +299,11 @@ template <int D, int QT, bool MASKED, int MASK>
 __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][Geo<D, QT>::W],
                                           const uint32_t (&vb)[Geo<D, QT>::NS][Geo<D, QT>::W],
                                           const uint32_t (&qr)[QT][Geo<D, QT>::W], float c,
-                                          float lazy, State<D, QT> &st, int key0,
+                                          float lazy, State<D, QT> &st, int key0, int delta,
                                           const int (&lim)[QT], int tb, const uint64_t (&anc)[QT])
 {
     using G = Geo<D, QT>;
-    constexpr int NS = G::NS, W = G::W, DPL = G::DPL, KPS = G::KPS;
+    constexpr int NS = G::NS, W = G::W, DPL = G::DPL, KPS = G::KPS, OPL = G::OPL;
     float s[QT][NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
@@ -280,7 +359,7 @@ __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][G
             st.thr[v] = uniform(up ? tm + lazy : st.thr[v]);
             st.l[v] *= alpha;
 #pragma unroll
-            for (int d = 0; d < DPL; ++d)
+            for (int d = 0; d < OPL; ++d)
                 st.o[v][d] *= alpha;
         }
     }
@@ -293,6 +372,48 @@ __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][G
             s[v][j] = p;
         }
     }
+    if constexpr (G::PAIR) {
+        // value product over the key pair: vb[j][0 .. WV) holds the kept
+        // half of this lane's key, vb[j][WV .. W) the same dims of the
+        // partner's key; v_perm builds (own, partner) pairs per dim and one
+        // v_dot2_f32_bf16 adds both keys' terms with bf16 weights
+        constexpr int WV = G::WV;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            uint32_t pa[WV], pb[WV];
+#pragma unroll
+            for (int w = 0; w < WV; ++w) {
+                pa[w] = __builtin_amdgcn_perm(vb[j][WV + w], vb[j][w], 0x05040100u);
+                pb[w] = __builtin_amdgcn_perm(vb[j][WV + w], vb[j][w], 0x07060302u);
+            }
+#pragma unroll
+            for (int v = 0; v < QT; ++v) {
+                // the partner key's weight (row_ror:8 reads a lane of the
+                // same row in every lane, so no old value is needed)
+                const float pp = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s[v][j]), 0x128, 0xF, 0xF, true));
+                const uint32_t pk = pack_bf16(s[v][j], pp);
+                if constexpr (MASKED) {
+                    // a key this query vector may not see has weight 0; its
+                    // value half is cleared too, so a NaN there cannot leak
+                    const int key = key0 + KPS * j;
+                    const uint32_t keep =
+                        (row_sees<MASK>(key, lim[v], tb, anc[v]) ? 0x0000FFFFu : 0u) |
+                        (row_sees<MASK>(key + delta, lim[v], tb, anc[v]) ? 0xFFFF0000u : 0u);
+#pragma unroll
+                    for (int w = 0; w < WV; ++w) {
+                        st.o[v][2 * w] = dot2_acc(pk, pa[w] & keep, st.o[v][2 * w]);
+                        st.o[v][2 * w + 1] = dot2_acc(pk, pb[w] & keep, st.o[v][2 * w + 1]);
+                    }
+                } else {
+#pragma unroll
+                    for (int w = 0; w < WV; ++w) {
+                        st.o[v][2 * w] = dot2_acc(pk, pa[w], st.o[v][2 * w]);
+                        st.o[v][2 * w + 1] = dot2_acc(pk, pb[w], st.o[v][2 * w + 1]);
+                    }
+                }
+            }
+        }
+    } else {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         float vf[DPL];
@@ -317,6 +438,7 @@ __device__ __forceinline__ void fold_tile(const uint32_t (&kb)[Geo<D, QT>::NS][G
                     st.o[v][d] = fmaf(s[v][j], vf[d], st.o[v][d]);
             }
         }
+    }
     }
 }
 
@@ -345,6 +467,10 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int kg = lane / LPK;
     const int sl = lane % LPK;
+    // pair mode: key groups 2i and 2i+1 are partners
+    const int odd = kg & 1;
+    const int delta = odd ? -1 : 1;
+    const uint32_t lane_v = G::PAIR ? pair_lane_bytes<D, QT>(sl, odd) : 0u;
 
     const tf_segment &sd = p.segs[seg_i];
     Seg s;
@@ -372,19 +498,9 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
             report(p.err, TF_ERR_BAD_ROWS);
         return;
     }
-    int errbits = 0;
-    if constexpr (KIND == TF_KV_PAGED) {
-        if (s.pages == nullptr || s.capacity < 0 ||
-            (int64_t)s.key_count > ((int64_t)s.capacity << p.page_shift))
-            errbits |= TF_ERR_PAST_PAGES;
-    } else {
-        if (s.key_count > s.capacity)
-            errbits |= TF_ERR_PAST_PAGES;
-    }
-    if constexpr (KIND == TF_KV_RING) {
-        if (s.first < 0 || s.first >= s.capacity)
-            errbits |= TF_ERR_BAD_RING;
-    }
+    // hints, storage bounds, ring start; any of them: no key is read and the
+    // segment's rows are written as NaN
+    int errbits = segment_errors<KIND>(p, sd, D);
     const int n_splits = p.split_keys > 0 ? (s.key_count + p.split_keys - 1) / p.split_keys : 1;
     if (t >= n_splits)
         return;   // block-uniform: this grid cell has no split of this segment
@@ -468,6 +584,8 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
             const int key = tile_key0(i) + kg;
             a.cap = s.capacity;
             a.lane_b = lane_b;
+            a.delta = delta;
+            a.lane_v = lane_v;
             if constexpr (KIND == TF_KV_PAGED) {
                 int page = __builtin_amdgcn_readlane(pid, i & 63);
                 if ((unsigned)page >= (unsigned)p.pool_pages) {
@@ -477,7 +595,7 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
                 const size_t run = ((size_t)page * p.hkv + g) * p.page_size * (D * 2);
                 a.kbase = reinterpret_cast<const char *>(s.k) + run;
                 a.vbase = reinterpret_cast<const char *>(s.v) + run;
-                a.off0 = (uint32_t)(key & (p.page_size - 1)) * (D * 2) + lane_b;
+                a.off0 = (uint32_t)(key & (p.page_size - 1)) * (D * 2);
             } else {
                 const size_t head = (size_t)g * s.capacity * (D * 2);
                 a.kbase = reinterpret_cast<const char *>(s.k) + head;
@@ -498,10 +616,20 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
                 const uint32_t off = a.at(j);
                 load_row<D, QT, true>(kb[j], a.kbase, off);
             }
+            if constexpr (G::PAIR) {
+                // the kept half of this key's value row, then the same half
+                // of the partner key's row
 #pragma unroll
-            for (int j = 0; j < NS; ++j) {
-                const uint32_t off = a.at(j);
-                load_row<D, QT, true>(vb[j], a.vbase, off);
+                for (int j = 0; j < NS; ++j) {
+                    load_half<D, QT>(&vb[j][0], a.vbase, a.row_at(j, 0, a.lane_v));
+                    load_half<D, QT>(&vb[j][G::WV], a.vbase, a.row_at(j, a.delta, a.lane_v));
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NS; ++j) {
+                    const uint32_t off = a.at(j);
+                    load_row<D, QT, true>(vb[j], a.vbase, off);
+                }
             }
             // keep the issue order tile by tile (K, then V): the waits before
             // each fold count loads in issue order
@@ -526,22 +654,31 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
 #pragma unroll
             for (int u = 0; u < CH; ++u)
                 load_tile(kb[u], vb[u], min(b0 + u, b1 - 1));
-            for (int i0 = b0; i0 < b1; i0 += CH) {
+            // whole groups of CH tiles: no guard inside the hot loop (a
+            // guarded fold made the compiler keep two copies of the state)
+            int i0 = b0;
+            for (; i0 + CH <= b1; i0 += CH) {
 #pragma unroll
                 for (int u = 0; u < CH; ++u) {
                     const int i = i0 + u;
-                    if (i < b1)
-                        fold_tile<D, QT, false, MASK>(kb[u], vb[u], qr, c, lazy, st, tile_key0(i) + kg, lim, tb, anc);
+                    fold_tile<D, QT, false, MASK>(kb[u], vb[u], qr, c, lazy, st, tile_key0(i) + kg, delta,
+                                                  lim, tb, anc);
                     load_tile(kb[u], vb[u], min(i + CH, b1 - 1));
                 }
             }
+            // the last b1 - i0 < CH tiles are in kb[0 ..]
+#pragma unroll
+            for (int u = 0; u < CH - 1; ++u)
+                if (i0 + u < b1)
+                    fold_tile<D, QT, false, MASK>(kb[u], vb[u], qr, c, lazy, st, tile_key0(i0 + u) + kg, delta,
+                                                  lim, tb, anc);
         }
         for (int i = my_full; i < my_tiles; ++i) {
             if (i == my_full || (i & 63) == 0)
                 load_pids(i & ~63);
             uint32_t kb[NS][W], vb[NS][W];
             load_tile(kb, vb, i);
-            fold_tile<D, QT, true, MASK>(kb, vb, qr, c, lazy, st, tile_key0(i) + kg, lim, tb, anc);
+            fold_tile<D, QT, true, MASK>(kb, vb, qr, c, lazy, st, tile_key0(i) + kg, delta, lim, tb, anc);
         }
         if (page_bad) {
             if (lane == 0)
@@ -578,14 +715,24 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
         for (int v = 0; v < QT; ++v) {
             const float lv = fold(st.l[v], false);
             const float lov = fold(st.lo[v], true);
-#pragma unroll
-            for (int d = 0; d < DPL; ++d)
-                st.o[v][d] = fold(st.o[v][d], false);
-            if (writer) {
-                store_f32<D, QT>(xo[wave][v][rg], st.o[v], sl);
-                if (sl == 0) {
+            if constexpr (G::PAIR) {
+                // each 16-lane row already holds its key pair's whole output,
+                // half a slice per lane
+                store_pair_f32<D, QT>(xo[wave][v][rg], st.o[v], sl, odd);
+                if (writer && sl == 0) {
                     xl[wave][v][rg][0] = lv;
                     xl[wave][v][rg][1] = lov;
+                }
+            } else {
+#pragma unroll
+                for (int d = 0; d < DPL; ++d)
+                    st.o[v][d] = fold(st.o[v][d], false);
+                if (writer) {
+                    store_f32<D, QT>(xo[wave][v][rg], st.o[v], sl);
+                    if (sl == 0) {
+                        xl[wave][v][rg][0] = lv;
+                        xl[wave][v][rg][1] = lov;
+                    }
                 }
             }
             if (lane == 0)

@@ -213,6 +213,18 @@ def test_check_segments_host_rules():
     assert binding.tf_check_segments(_args(kind=binding.TF_KV_RING, total_rows=1), ring_past) == binding.TF_E_PAST_PAGES
 
 
+def test_check_segments_storage_limit():
+    # one kv head's run of a CONTIG / RING buffer must stay below 4 GiB (the
+    # kernels address it with 32-bit offsets): 2^23 slots at D 256 is 4 GiB
+    for kind in (binding.TF_KV_CONTIG, binding.TF_KV_RING):
+        big = _host_table([(1 << 23, 0, 0, 1, 40)], kind=kind)
+        a = _args(kind=kind, total_rows=1)
+        a.head_dim = 256
+        assert binding.tf_check_segments(a, big) == binding.TF_E_UNSUPPORTED
+        fits = _host_table([((1 << 23) - 1, 0, 0, 1, 40)], kind=kind)
+        assert binding.tf_check_segments(a, fits) == binding.TF_OK
+
+
 def test_check_segments_workspace():
     t = _host_table([(4, 0, 0, 1, 100)])
     t[0].partial_offset = 0

@@ -258,6 +258,12 @@ def test_different_split_sizes_agree_within_tolerance(gpu):
 
 
 def test_partial_records_match_oracle_partials(gpu):
+    # m is a reference and l, o are relative to it: the log-sum-exp and o / l
+    # are what a record fixes.  The value products take the weights rounded
+    # to bf16 (relative error <= 2^-9 each, sums in fp32), so o / l may differ
+    # from the float64 result by at most 2^-9 * max |v| over the split's keys
+    # (a weighted mean of per-key errors 2^-9 p_j |v_jd| / l); the test allows
+    # that plus 1e-5.
     split = 64
     w = synth.make_workload("parts", synth.KIND_PAGED, 8, 2, 128, [3, 1], [200, 130], seed=14,
                             page_size=32, pool_pages=20, split_keys=split)
@@ -283,7 +289,10 @@ def test_partial_records_match_oracle_partials(gpu):
                     assert mr - 8 * np.log(2) - 1e-5 <= rec[0] <= mr + 1e-5 * max(1.0, abs(mr))
                     lse_g, lse_r = rec[0] + np.log(rec[1]), mr + np.log(lr)
                     assert abs(lse_g - lse_r) <= 1e-5 * max(1.0, abs(lse_r))
-                    assert np.max(np.abs(rec[4:] / rec[1] - orr / lr)) <= 1e-5
+                    si = w.segments.index(seg)
+                    vk = synth.bf16_bits_to_f32(w.v_logical[si][t * split:(t + 1) * split, h // 4]).astype(np.float64)
+                    bound = 1e-5 + 2.0 ** -9 * np.max(np.abs(vk), axis=0)
+                    assert np.all(np.abs(rec[4:] / rec[1] - orr / lr) <= bound)
             row += 1
 
 
@@ -393,6 +402,66 @@ def test_key_count_past_pages_sets_error(gpu):
     s2 = w.segments[2]
     assert np.isnan(got[s2.row_offset:s2.row_offset + s2.n_rows]).all()
     assert np.isfinite(got[:s2.row_offset]).all()
+
+
+def test_segment_past_the_hints_sets_error_and_nan(gpu):
+    # key_count above max_keys (decode segments) and n_rows above max_rows
+    # (a matrix-core segment): the grid does not cover them; the rows it
+    # covers are NaN, rows past max_rows are not written, the others are fine
+    w = synth.make_workload("hints", synth.KIND_PAGED, 8, 2, 128, [1, 20, 1], [700, 900, 1500], seed=33,
+                            page_size=32, pool_pages=120, split_keys=256)
+    ref = oracle.attn_workload(w)
+    dw = launch.DeviceWorkload(w, gpu)
+    a = dw.args(0)
+    a.max_keys = 1400        # segment 2 holds 1500 keys
+    a.max_rows = 12          # segment 1 has 20 rows
+    a.min_rows = 0
+    dw.out.fill_(0x7FA5)
+    st = __import__("torch").cuda.current_stream(gpu).cuda_stream
+    assert binding.tf_attn_rows(a, st) == binding.TF_OK
+    assert binding.tf_attn_merge(a, st) == binding.TF_OK
+    got = dw.output()
+    assert dw.error_word() == binding.TF_ERR_HINTS
+    s0, s1, s2 = w.segments
+    assert_close(got[s0.row_offset:s0.row_offset + 1], ref[s0.row_offset:s0.row_offset + 1], what="in-bounds segment")
+    assert np.isnan(f32(got[s2.row_offset])).all()
+    assert np.isnan(f32(got[s1.row_offset:s1.row_offset + 12])).all()
+    assert np.all(got[s1.row_offset + 12:s1.row_offset + 20] == 0x7FA5), "rows past max_rows were written"
+
+
+@pytest.mark.parametrize("kind", ["contig", "ring"])
+def test_buffer_past_32bit_offsets_sets_error(gpu, kind):
+    # one kv head's run of 2^23 keys x D 256 x 2 bytes = 4 GiB: the kernels'
+    # 32-bit offsets cannot address it, so the segment is refused on the
+    # device (no key is read) and its rows are NaN.  The buffers are really
+    # that large, so no access could leave them either way.
+    import torch
+    cap = 1 << 23
+    w = synth.make_workload("big", synth.KIND_CONTIG, 4, 1, 256, [1], [64], seed=34, split_keys=0,
+                            contig_capacity=[80])
+    k = torch.zeros(cap * 256, dtype=torch.int16, device=gpu)
+    v = torch.zeros(cap * 256, dtype=torch.int16, device=gpu)
+    q = launch._dev(w.q, gpu)
+    out = torch.full((1, 4, 256), 0x7FA5, dtype=torch.int16, device=gpu)
+    err = torch.zeros(1, dtype=torch.int32, device=gpu)
+    seg = (binding.tf_segment * 1)()
+    seg[0].k, seg[0].v, seg[0].pages = k.data_ptr(), v.data_ptr(), None
+    seg[0].capacity, seg[0].first, seg[0].row_offset, seg[0].n_rows, seg[0].key_count = cap, 0, 0, 1, 64
+    seg[0].partial_offset = 0
+    table = torch.frombuffer(bytearray(bytes(__import__("ctypes").string_at(
+        __import__("ctypes").addressof(seg), __import__("ctypes").sizeof(seg)))), dtype=torch.uint8).to(gpu)
+    a = binding.tf_attn_args()
+    a.kind = binding.KIND_CODE[kind]
+    a.n_segments, a.total_rows, a.max_rows, a.max_keys, a.min_rows = 1, 1, 1, 64, 1
+    a.n_q_heads, a.n_kv_heads, a.head_dim, a.page_size, a.pool_pages = 4, 1, 256, 0, 0
+    a.split_keys, a.scale, a.mask = 0, w.scale, binding.TF_MASK_CAUSAL
+    a.segs, a.tree, a.q, a.out = table.data_ptr(), None, q.data_ptr(), out.data_ptr()
+    a.partials, a.partials_bytes, a.err = None, 0, err.data_ptr()
+    assert binding.tf_check_segments(a, seg) == binding.TF_E_UNSUPPORTED
+    assert binding.tf_attn_rows(a, torch.cuda.current_stream(gpu).cuda_stream) == binding.TF_OK
+    torch.cuda.synchronize()
+    assert int(err.item()) & binding.TF_ERR_STORAGE
+    assert np.isnan(f32(launch.to_host_u16(out))).all()
 
 
 def test_argmax_small_cases(gpu):
