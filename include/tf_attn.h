@@ -205,6 +205,24 @@ int tf_attn_rows(const tf_attn_args *a, hipStream_t stream);
 int tf_attn_merge(const tf_attn_args *a, hipStream_t stream);
 
 /*
+ * tf_attn_static: for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The same as tf_attn_rows followed, when split_keys > 0, by tf_attn_merge,
+ * except that the split partials live in a device array the library owns
+ * (TF_STATIC_PARTIALS_BYTES bytes on each device it runs on, held until the
+ * process ends) instead of a caller workspace.  a->partials must be NULL
+ * (TF_E_INVALID otherwise); a->partials_bytes is the size tf_plan_partials
+ * returned for the table and must be at most TF_STATIC_PARTIALS_BYTES
+ * (TF_E_WORKSPACE otherwise).  The call allocates nothing.  Every call on a
+ * device shares that device's array, which keeps the last call's records:
+ * calls that overlap on one GPU (other streams, other threads) race.  Same
+ * return codes and device error bits as tf_attn_rows / tf_attn_merge;
+ * TF_E_LAUNCH also if the array's address cannot be obtained.
+ */
+#define TF_STATIC_PARTIALS_BYTES ((size_t)16 << 20)
+int tf_attn_static(const tf_attn_args *a, hipStream_t stream);
+
+/*
  * tf_argmax: for each row of bf16 logits (row i starts at logits + i *
  * row_stride elements; the first `vocab` are read) writes ids[i], the lowest
  * id among the largest values, and flags[i] = 1 if any of the row's logits is

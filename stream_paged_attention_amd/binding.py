@@ -35,7 +35,9 @@ TF_ERR_BAD_LAYER = 32
 TF_ERR_HINTS = 64
 TF_ERR_STORAGE = 128
 
-EXPORTS = ("tf_attn_rows", "tf_attn_merge", "tf_argmax", "tf_argmax_workspace_bytes",
+TF_STATIC_PARTIALS_BYTES = 16 << 20
+
+EXPORTS = ("tf_attn_rows", "tf_attn_merge", "tf_attn_static", "tf_argmax", "tf_argmax_workspace_bytes",
            "tf_kv_put", "tf_state_save", "tf_state_restore", "tf_plan_partials",
            "tf_check_segments", "tf_strerror")
 
@@ -103,6 +105,8 @@ def load(path: str = LIB_PATH):
     lib.tf_attn_rows.argtypes = [ctypes.POINTER(tf_attn_args), vp]
     lib.tf_attn_merge.restype = ctypes.c_int
     lib.tf_attn_merge.argtypes = [ctypes.POINTER(tf_attn_args), vp]
+    lib.tf_attn_static.restype = ctypes.c_int
+    lib.tf_attn_static.argtypes = [ctypes.POINTER(tf_attn_args), vp]
     lib.tf_argmax.restype = ctypes.c_int
     lib.tf_argmax.argtypes = [vp, i32, i32, ctypes.c_int64, vp, vp, vp, sz, vp]
     lib.tf_argmax_workspace_bytes.restype = sz
@@ -130,6 +134,10 @@ def tf_attn_rows(args: tf_attn_args, stream: int, lib=None) -> int:
 
 def tf_attn_merge(args: tf_attn_args, stream: int, lib=None) -> int:
     return (lib or load()).tf_attn_merge(ctypes.byref(args), ctypes.c_void_p(stream))
+
+
+def tf_attn_static(args: tf_attn_args, stream: int, lib=None) -> int:
+    return (lib or load()).tf_attn_static(ctypes.byref(args), ctypes.c_void_p(stream))
 
 
 def tf_argmax(logits: int, n_rows: int, vocab: int, row_stride: int, ids: int, flags: int,
