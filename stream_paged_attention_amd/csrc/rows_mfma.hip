@@ -19,10 +19,9 @@
 // and
 //     O^T += V^T P^T       (A = V^T from ds_read_tr16_b64, B = P^T in bf16)
 // where P^T is exactly the S^T register layout: no lane exchange between
-// the two products.  P is carried as two bf16 terms (its rounding and the
-// remainder), each multiplied in, so the weights keep ~16 bits.  Products
-// against a block of ones accumulate l = sum p (the same two terms) next
-// to O.
+// the two products.  P is rounded to bf16 (fp32 sums); a product against a
+// block of ones accumulates l = sum p from the same rounded weights next to
+// O.
 //
 // K/V tiles are staged through LDS by direct global->LDS loads (16 bytes a
 // lane, 1 KB a wave instruction), double buffered: the next tile's loads are
@@ -427,7 +426,7 @@ __attribute__((amdgpu_waves_per_eu(SMALL ? 2 : 1))) void rows_mfma_kernel(RowsPa
             }
 
             // -- online softmax per vector; P^T fragments in bf16
-            u32x4_t pf[NQB], pl[NQB];   // P^T in bf16: rounded value and its remainder
+            u32x4_t pf[NQB];   // P^T rounded to bf16
             uint64_t need = 0;
             float tmax[NQB];
 #pragma unroll
@@ -486,20 +485,12 @@ __attribute__((amdgpu_waves_per_eu(SMALL ? 2 : 1))) void rows_mfma_kernel(RowsPa
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         pe[kb * 4 + e] = exp2_fast(fmaf(s[b][kb][e], c, -mc[b]));
-                // p = hi + lo, both bf16: the value product takes the two parts, so
-                // the weights keep about 16 significant bits instead of 8
-                float pr[8];
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    pf[b][w] = pack_bf16(pe[2 * w], pe[2 * w + 1]);
-                    pr[2 * w] = pe[2 * w] - bf16_lo(pf[b][w]);
-                    pr[2 * w + 1] = pe[2 * w + 1] - bf16_hi(pf[b][w]);
-                }
+                // the weights rounded to bf16 (fp32 sums): the value product and
+                // l take the same rounded weights
 #pragma unroll
                 for (int w = 0; w < 4; ++w)
-                    pl[b][w] = pack_bf16(pr[2 * w], pr[2 * w + 1]);
+                    pf[b][w] = pack_bf16(pe[2 * w], pe[2 * w + 1]);
                 lsum[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, as_bf16x8(pf[b]), lsum[b], 0, 0, 0);
-                lsum[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, as_bf16x8(pl[b]), lsum[b], 0, 0, 0);
             }
 
             // -- values: O^T += V^T P^T per 16-dim block.  V^T fragment of lane
@@ -522,20 +513,13 @@ __attribute__((amdgpu_waves_per_eu(SMALL ? 2 : 1))) void rows_mfma_kernel(RowsPa
                                (uint32_t)(uint16_t)h1[0] | ((uint32_t)(uint16_t)h1[1] << 16),
                                (uint32_t)(uint16_t)h1[2] | ((uint32_t)(uint16_t)h1[3] << 16)};
             };
-            // the products of two dim blocks: the rounded and the remainder
-            // terms of one block are not back to back (independent chains)
+            // the products of two dim blocks (independent chains)
             auto pv2 = [&](int db, const u32x4_t &v0, const u32x4_t &v1) {
 #pragma unroll
                 for (int b = 0; b < NQB; ++b) {
                     o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v0), as_bf16x8(pf[b]), o[b][db], 0, 0, 0);
                     o[b][db + 1] =
                         __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v1), as_bf16x8(pf[b]), o[b][db + 1], 0, 0, 0);
-                }
-#pragma unroll
-                for (int b = 0; b < NQB; ++b) {
-                    o[b][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v0), as_bf16x8(pl[b]), o[b][db], 0, 0, 0);
-                    o[b][db + 1] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v1), as_bf16x8(pl[b]), o[b][db + 1], 0, 0, 0);
                 }
             };
             // masked tile: nonfinite values become 0 (exponent all ones -> zero)

@@ -14,7 +14,7 @@ import pytest
 
 from oracle import oracle
 from stream_paged_attention_amd import binding, launch, synth
-from tests.test_gpu_parity import REL_SMALL, assert_close, f32
+from tests.test_gpu_parity import REL_SMALL, assert_close, f32, weight_allowance
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,8 @@ def test_mask_matches_oracle_and_per_segment(gpu, mask, kind, d, hq, hkv, rows, 
     assert dw.check_table() == binding.TF_OK
     dw.run()
     batched = dw.output()
-    assert_close(batched, oracle.attn_workload(w), rel=REL_SMALL, what=f"{mask} mask")
+    ref = oracle.attn_workload(w)
+    assert_close(batched, ref, rel=REL_SMALL, what=f"{mask} mask", extra=weight_allowance(w, ref))
     assert dw.error_word() == 0
     assert np.array_equal(batched, dw.run_per_segment()), "batched launch differs from per-segment"
 
@@ -94,7 +95,8 @@ def test_full_mask_reads_the_newest_key_from_every_row(gpu):
     dw = launch.DeviceWorkload(w, gpu)
     dw.run()
     got = f32(dw.output())
-    assert_close(dw.output(), oracle.attn_workload(w), rel=REL_SMALL, what="full NaN")
+    ref = oracle.attn_workload(w)
+    assert_close(dw.output(), ref, rel=REL_SMALL, what="full NaN", extra=weight_allowance(w, ref))
     assert np.isnan(got[:, 8:16]).all() and np.isfinite(got[:, 0:8]).all()
 
 
@@ -109,7 +111,8 @@ def test_tree_never_reads_a_sibling_key(gpu, hq):
     dw = launch.DeviceWorkload(w, gpu)
     dw.run()
     got = f32(dw.output())
-    assert_close(dw.output(), oracle.attn_workload(w), rel=REL_SMALL, what="tree NaN")
+    ref = oracle.attn_workload(w)
+    assert_close(dw.output(), ref, rel=REL_SMALL, what="tree NaN", extra=weight_allowance(w, ref))
     assert np.isnan(got[2]).all() and np.isfinite(got[[0, 1, 3]]).all()
 
 
@@ -132,4 +135,6 @@ def test_tree_segment_past_64_rows_sets_error(gpu):
     ref = oracle.attn([3], [50], w.q[65:], [w.k_logical[1]],
                       [w.v_logical[1]], n_q_heads=8, n_kv_heads=2, head_dim=128, scale=w.scale,
                       mask="tree", tree=np.zeros(3, dtype=np.uint64))
-    assert_close(got[65:], ref, rel=REL_SMALL, what="tree segment after a refused one")
+    v1 = np.abs(synth.bf16_bits_to_f32(w.v_logical[1]).astype(np.float64)).max(axis=0)   # [Hkv][D]
+    extra = 2.0 ** -9 * (np.repeat(v1, 4, axis=0)[None] + np.abs(ref))
+    assert_close(got[65:], ref, rel=REL_SMALL, what="tree segment after a refused one", extra=extra)

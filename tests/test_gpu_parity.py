@@ -22,7 +22,7 @@ def f32(bits):
     return synth.bf16_bits_to_f32(bits).astype(np.float64)
 
 
-def assert_close(got_bits, ref, tol=2e-3, rel=0.0, what=""):
+def assert_close(got_bits, ref, tol=2e-3, rel=0.0, what="", extra=None):
     got = f32(got_bits)
     assert got.shape == ref.shape
     nan_g, nan_r = np.isnan(got), np.isnan(ref)
@@ -30,12 +30,35 @@ def assert_close(got_bits, ref, tol=2e-3, rel=0.0, what=""):
     fin = ~nan_r
     err = np.abs(got[fin] - ref[fin])
     bound = tol + rel * np.abs(ref[fin])
+    if extra is not None:
+        bound = bound + extra[fin]
     worst = float(np.max(err - bound)) if err.size else -1.0
     assert worst <= 0.0, f"{what}: max |err| {float(err.max()):.3e} exceeds the bound"
     return float(err.max()) if err.size else 0.0
 
 
 REL_SMALL = 2.0 ** -8
+
+
+def weight_allowance(w, ref):
+    """Per output element, what rounding the attention weights to bf16 may
+    move it: the weights enter the value products (and l) with a relative
+    error of at most 2^-9 each and are normalised by the same rounded sum, so
+    the output is a convex combination of the visible values with perturbed
+    weights, |delta| <= 2^-9 * max_j |v_j - out| <= 2^-9 * (max_j |v_j| +
+    |out|).  max_j runs over all of the segment's keys (a superset of those a
+    row sees) and over finite values (nonfinite ones are handled by the NaN
+    rule and compared apart).  It matters only where a row sees few keys; the
+    five synthetic workloads are held to 2e-3 without it."""
+    extra = np.zeros(ref.shape)
+    group = w.n_q_heads // w.n_kv_heads
+    for si, s in enumerate(w.segments):
+        v = np.abs(synth.bf16_bits_to_f32(w.v_logical[si]).astype(np.float64))
+        v = np.where(np.isfinite(v), v, 0.0)
+        vmax = np.repeat(v.max(axis=0), group, axis=0)          # [Hq][D]
+        rows = slice(s.row_offset, s.row_offset + s.n_rows)
+        extra[rows] = 2.0 ** -9 * (vmax[None] + np.nan_to_num(np.abs(ref[rows]), posinf=0.0))
+    return extra
 
 
 @pytest.fixture(scope="module")
@@ -165,7 +188,7 @@ def test_poison_outside_ranges_changes_nothing(gpu):
         assert np.array_equal(pair[0], pair[1]), f"{kind}: NaN poison outside the range leaked"
         outs.append(pair[0])
     ref = oracle.attn_workload(w)
-    assert_close(outs[0], ref, rel=REL_SMALL, what="poisoned paged")
+    assert_close(outs[0], ref, rel=REL_SMALL, what="poisoned paged", extra=weight_allowance(w, ref))
 
 
 # --------------------------------------------------------------------------- shapes, splits, edges
@@ -219,7 +242,8 @@ def test_shapes_match_oracle(gpu, kind, d, hq, hkv, rows, keys, split):
     dw = launch.DeviceWorkload(w, gpu)
     assert dw.check_table() == binding.TF_OK
     dw.run()
-    assert_close(dw.output(), oracle.attn_workload(w), rel=REL_SMALL, what="shape")
+    ref = oracle.attn_workload(w)
+    assert_close(dw.output(), ref, rel=REL_SMALL, what="shape", extra=weight_allowance(w, ref))
     assert dw.error_word() == 0
 
 
@@ -244,7 +268,8 @@ def test_other_page_sizes(gpu, page_size, hq, hkv, d, rows, keys, split):
     dw = launch.DeviceWorkload(w, gpu)
     assert dw.check_table() == binding.TF_OK
     dw.run()
-    assert_close(dw.output(), oracle.attn_workload(w), rel=REL_SMALL, what=f"P{page_size}")
+    ref = oracle.attn_workload(w)
+    assert_close(dw.output(), ref, rel=REL_SMALL, what=f"P{page_size}", extra=weight_allowance(w, ref))
     assert dw.error_word() == 0
 
 
@@ -254,7 +279,7 @@ def test_different_split_sizes_agree_within_tolerance(gpu):
     for split in (0, 32, 128, 512):
         dw = launch.DeviceWorkload(w, gpu, split_keys=split)
         dw.run()
-        assert_close(dw.output(), ref, rel=REL_SMALL, what=f"split {split}")
+        assert_close(dw.output(), ref, rel=REL_SMALL, what=f"split {split}", extra=weight_allowance(w, ref))
 
 
 def test_partial_records_match_oracle_partials(gpu):
@@ -263,7 +288,8 @@ def test_partial_records_match_oracle_partials(gpu):
     # to bf16 (relative error <= 2^-9 each, sums in fp32), so o / l may differ
     # from the float64 result by at most 2^-9 * max |v| over the split's keys
     # (a weighted mean of per-key errors 2^-9 p_j |v_jd| / l); the test allows
-    # that plus 1e-5.
+    # that plus 1e-5.  Where l sums the rounded weights, the log-sum-exp moves
+    # by at most -log(1 - 2^-9).
     split = 64
     w = synth.make_workload("parts", synth.KIND_PAGED, 8, 2, 128, [3, 1], [200, 130], seed=14,
                             page_size=32, pool_pages=20, split_keys=split)
@@ -288,7 +314,9 @@ def test_partial_records_match_oracle_partials(gpu):
                     # 8 ln 2 below their max; the log-sum-exp and o / l are fixed
                     assert mr - 8 * np.log(2) - 1e-5 <= rec[0] <= mr + 1e-5 * max(1.0, abs(mr))
                     lse_g, lse_r = rec[0] + np.log(rec[1]), mr + np.log(lr)
-                    assert abs(lse_g - lse_r) <= 1e-5 * max(1.0, abs(lse_r))
+                    # l may be the sum of the bf16-rounded weights (the matrix-core
+                    # kernel): |log l - log sum p| <= -log(1 - 2^-9)
+                    assert abs(lse_g - lse_r) <= 1e-5 * max(1.0, abs(lse_r)) - np.log1p(-2.0 ** -9)
                     si = w.segments.index(seg)
                     vk = synth.bf16_bits_to_f32(w.v_logical[si][t * split:(t + 1) * split, h // 4]).astype(np.float64)
                     bound = 1e-5 + 2.0 ** -9 * np.max(np.abs(vk), axis=0)
@@ -306,7 +334,7 @@ def _nan_case(gpu, plant):
     dw = launch.DeviceWorkload(w2, gpu)
     dw.run()
     got, ref = dw.output(), oracle.attn_workload(w2)
-    assert_close(got, ref, rel=REL_SMALL, what="nan rule")
+    assert_close(got, ref, rel=REL_SMALL, what="nan rule", extra=weight_allowance(w2, ref))
     return f32(got)
 
 
@@ -347,7 +375,7 @@ def test_nan_value_reaches_its_lane_when_waves_split_dims(gpu, d, hq, hkv, rows,
     dw = launch.DeviceWorkload(w2, gpu)
     dw.run()
     got, ref = dw.output(), oracle.attn_workload(w2)
-    assert_close(got, ref, rel=REL_SMALL, what="nan split dims")
+    assert_close(got, ref, rel=REL_SMALL, what="nan split dims", extra=weight_allowance(w2, ref))
     g = f32(got)[:rows]       # the first segment's rows
     group = hq // hkv
     assert np.isnan(g[:, 0:group, dim]).all()
