@@ -254,7 +254,7 @@ class AttnStep:
             self.ids = torch.empty(self.nrows, dtype=torch.int32, device=dev)
             self.flags = torch.empty(self.nrows, dtype=torch.uint8, device=dev)
             self.wsb = binding.tf_argmax_workspace_bytes(self.nrows, self.vocab)
-            self.ws = torch.empty(self.wsb // 8 + 1, dtype=torch.int64, device=dev)
+            self.ws = torch.zeros(self.wsb // 8 + 1, dtype=torch.int64, device=dev)   # zero before first use
 
     def attn(self, i: int) -> int:
         a = self.argl[i % self.copies]

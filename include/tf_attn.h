@@ -227,11 +227,14 @@ int tf_attn_static(const tf_attn_args *a, hipStream_t stream);
  * row_stride elements; the first `vocab` are read) writes ids[i], the lowest
  * id among the largest values, and flags[i] = 1 if any of the row's logits is
  * NaN or +-Inf (else 0).  NaN ranks as -inf for the id, +0.0 equals -0.0
- * (TensorFold PR #1503, the lfm2_argmax commit and the router note).
- * workspace: device memory of at least tf_argmax_workspace_bytes(n_rows,
- * vocab) bytes, contents ignored on entry.  Returns TF_E_INVALID for null
- * pointers, vocab < 1, row_stride < vocab; TF_E_WORKSPACE if the workspace is
- * too small.
+ * (TensorFold PR #1503, the lfm2_argmax commit and the router note).  One
+ * launch.  workspace: device memory of at least tf_argmax_workspace_bytes(
+ * n_rows, vocab) bytes (16 per row, 8-byte aligned) that holds zeros before
+ * its first use; every call leaves it all zero again, so one zeroed
+ * allocation serves every later call.  Calls that share a workspace must not
+ * overlap.  Returns TF_E_INVALID for null pointers, vocab < 1, row_stride <
+ * vocab; TF_E_WORKSPACE if the workspace is too small; TF_E_UNSUPPORTED for a
+ * vocabulary of more than 65535 * 8192 logits.
  */
 int tf_argmax(const void *logits, int32_t n_rows, int32_t vocab, int64_t row_stride,
               int32_t *ids, uint8_t *flags, void *workspace, size_t workspace_bytes,
@@ -321,7 +324,7 @@ typedef struct tf_state_args {
 int tf_state_save(const tf_state_args *a, hipStream_t stream);
 int tf_state_restore(const tf_state_args *a, hipStream_t stream);
 
-/* Workspace bytes tf_argmax needs for n_rows rows of vocab logits. */
+/* Workspace bytes tf_argmax needs for n_rows rows of vocab logits (zeroed once by the caller). */
 size_t tf_argmax_workspace_bytes(int32_t n_rows, int32_t vocab);
 
 /*

@@ -18,6 +18,7 @@ hipError_t launch_merge(const RowsParams &p, int head_dim, int max_rows, hipStre
 hipError_t launch_argmax(const uint16_t *logits, int n_rows, int vocab, int64_t row_stride,
                          int32_t *ids, uint8_t *flags, void *workspace, hipStream_t st);
 int argmax_chunk_count(int vocab);
+size_t argmax_slot_bytes();
 }  // namespace tfa
 
 namespace {
@@ -289,8 +290,7 @@ size_t tf_argmax_workspace_bytes(int32_t n_rows, int32_t vocab)
 {
     if (n_rows <= 0 || vocab <= 0)
         return 0;
-    const int64_t cells = (int64_t)n_rows * tfa::argmax_chunk_count(vocab);
-    return (size_t)(cells * (int64_t)(sizeof(uint64_t) + sizeof(uint32_t)));
+    return (size_t)n_rows * tfa::argmax_slot_bytes();
 }
 
 int tf_argmax(const void *logits, int32_t n_rows, int32_t vocab, int64_t row_stride, int32_t *ids,
@@ -309,6 +309,8 @@ int tf_argmax(const void *logits, int32_t n_rows, int32_t vocab, int64_t row_str
         return TF_E_WORKSPACE;
     if ((int64_t)n_rows * tfa::argmax_chunk_count(vocab) > 0x7FFFFFFF)
         return TF_E_INVALID;
+    if (tfa::argmax_chunk_count(vocab) > 0xFFFF)
+        return TF_E_UNSUPPORTED;   // a row's chunk count must fit the counter's 16 bits
     if (tfa::launch_argmax(static_cast<const uint16_t *>(logits), n_rows, vocab, row_stride, ids, flags,
                            workspace, stream) != hipSuccess)
         return TF_E_LAUNCH;

@@ -7,10 +7,13 @@
 // unsigned 16-bit rank (NaN taken as -inf, -0.0 as +0.0) above the complement
 // of its id, so the largest key is the largest value at the lowest id.  The
 // max of keys is order-independent, so the pick does not depend on how the
-// row is cut up.  Phase 1: one workgroup per (row, 8192-logit chunk) reduces
-// its chunk to a key and a flag.  Phase 2: one wave per row reduces the
-// chunks.  A row of one chunk (vocabularies up to 8192) is finished by
-// phase 1, which then writes the id and flag itself: one launch.
+// row is cut up.  One launch: one workgroup per (row, 8192-logit chunk)
+// reduces its chunk to a key and a flag.  A row of one chunk is finished
+// there.  Otherwise each chunk folds its key into the row's 64-bit slot of
+// the workspace with an atomic max, then counts itself (and its flag) into
+// the row's counter word; the chunk that completes the count reads the final
+// key back with an exchange that re-zeroes the slot, writes the id and flag,
+// and zeroes the counter: the workspace is left as it was found, all zero.
 #include "device.hpp"
 
 namespace tfa {
@@ -31,11 +34,19 @@ __device__ __forceinline__ uint32_t rank16(uint32_t b, uint32_t &nonfinite)
     return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
 }
 
+// A row's workspace slot: the largest chunk key so far and the count of
+// chunks done (low 16 bits) plus the count of chunks holding a nonfinite
+// logit (high 16 bits).  All zero between calls.
+struct RowSlot {
+    uint64_t key;
+    uint32_t count;
+    uint32_t pad;
+};
+
 __global__ __launch_bounds__(kThreads) void argmax_chunks(const uint16_t *logits, int vocab,
                                                           int64_t row_stride, int n_chunks,
-                                                          int vec_ok, uint64_t *keys,
-                                                          uint32_t *flags, int32_t *row_ids,
-                                                          uint8_t *row_flags)
+                                                          int vec_ok, RowSlot *slots,
+                                                          int32_t *row_ids, uint8_t *row_flags)
 {
     const int chunk = blockIdx.x % n_chunks;
     const int row = blockIdx.x / n_chunks;
@@ -92,38 +103,22 @@ __global__ __launch_bounds__(kThreads) void argmax_chunks(const uint16_t *logits
             return;
         }
         const uint64_t key = ((uint64_t)(best >> 16) << 32) | (uint64_t)(0xFFFFFFFFu - id);
-        keys[(int64_t)row * n_chunks + chunk] = key;
-        flags[(int64_t)row * n_chunks + chunk] = nonfinite;
-    }
-}
-
-__global__ __launch_bounds__(kThreads) void argmax_rows(int n_rows, int n_chunks,
-                                                        const uint64_t *keys,
-                                                        const uint32_t *cflags, int32_t *ids,
-                                                        uint8_t *flags)
-{
-    const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (row >= n_rows)
-        return;
-    uint64_t best = 0;
-    uint32_t nonfinite = 0;
-    for (int c = lane; c < n_chunks; c += 64) {
-        const uint64_t k = keys[(int64_t)row * n_chunks + c];
-        best = k > best ? k : best;
-        nonfinite |= cflags[(int64_t)row * n_chunks + c];
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best, off);
-        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), off);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        best = o > best ? o : best;
-        nonfinite |= (uint32_t)__shfl_xor((int)nonfinite, off);
-    }
-    if (lane == 0) {
-        ids[row] = (int32_t)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
-        flags[row] = nonfinite ? 1 : 0;
+        RowSlot *slot = slots + row;
+        __hip_atomic_fetch_max(&slot->key, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the max is performed (acknowledged) before this chunk is counted,
+        // so the chunk that sees the full count reads every chunk's key
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const uint32_t add = 1u + (nonfinite ? 0x10000u : 0u);
+        const uint32_t old = __hip_atomic_fetch_add(&slot->count, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((old & 0xFFFFu) == (uint32_t)(n_chunks - 1)) {
+            const uint64_t fin = __hip_atomic_exchange(&slot->key, (uint64_t)0, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&slot->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            row_ids[row] = (int32_t)(0xFFFFFFFFu - (uint32_t)(fin & 0xFFFFFFFFu));
+            row_flags[row] = ((old >> 16) + (nonfinite ? 1u : 0u)) != 0 ? 1 : 0;
+        }
     }
 }
 
@@ -131,19 +126,16 @@ __global__ __launch_bounds__(kThreads) void argmax_rows(int n_rows, int n_chunks
 
 int argmax_chunk_count(int vocab) { return (vocab + kChunk - 1) / kChunk; }
 
+size_t argmax_slot_bytes() { return sizeof(RowSlot); }
+
 hipError_t launch_argmax(const uint16_t *logits, int n_rows, int vocab, int64_t row_stride,
                          int32_t *ids, uint8_t *flags, void *workspace, hipStream_t st)
 {
     const int n_chunks = argmax_chunk_count(vocab);
-    uint64_t *keys = static_cast<uint64_t *>(workspace);
-    uint32_t *cflags = reinterpret_cast<uint32_t *>(keys + (int64_t)n_rows * n_chunks);
     const int vec_ok = ((reinterpret_cast<uintptr_t>(logits) & 15u) == 0 && (row_stride & 7) == 0) ? 1 : 0;
     hipLaunchKernelGGL(argmax_chunks, dim3((unsigned)(n_chunks * n_rows)), dim3(kThreads), 0, st,
-                       logits, vocab, row_stride, n_chunks, vec_ok, keys, cflags, ids, flags);
-    if (n_chunks == 1)
-        return hipGetLastError();
-    hipLaunchKernelGGL(argmax_rows, dim3((unsigned)((n_rows + 3) / 4)), dim3(kThreads), 0, st, n_rows,
-                       n_chunks, keys, cflags, ids, flags);
+                       logits, vocab, row_stride, n_chunks, vec_ok, static_cast<RowSlot *>(workspace), ids,
+                       flags);
     return hipGetLastError();
 }
 

@@ -250,7 +250,7 @@ def argmax(logits: np.ndarray, device="cuda:0", vocab: Optional[int] = None):
     ids = torch.full((rows,), -1, dtype=torch.int32, device=dev)
     flags = torch.full((rows,), 7, dtype=torch.uint8, device=dev)
     nbytes = binding.tf_argmax_workspace_bytes(rows, vocab)
-    ws = torch.empty(max(nbytes, 8) // 8 + 1, dtype=torch.int64, device=dev)
+    ws = torch.zeros(max(nbytes, 8) // 8 + 1, dtype=torch.int64, device=dev)   # zero before first use
     st = torch.cuda.current_stream(dev).cuda_stream
     check(binding.tf_argmax(x.data_ptr(), rows, vocab, stride, ids.data_ptr(), flags.data_ptr(),
                             ws.data_ptr(), nbytes, st), "tf_argmax")

@@ -70,6 +70,7 @@ def test_guards_untouched(gpu, name):
         fl_whole, fl_in, g_fl = guarded(rows, torch.uint8, PAT8, gpu)
         nbytes = binding.tf_argmax_workspace_bytes(rows, vocab)
         ws_whole, ws_in, g_ws = guarded(max(nbytes, 1), torch.uint8, PAT8, gpu)
+        ws_in.zero_()   # the workspace holds zeros before its first use
         st = torch.cuda.current_stream(gpu).cuda_stream
         for _ in range(2):
             rc = binding.tf_argmax(x.data_ptr(), rows, vocab, vocab, ids_in.data_ptr(), fl_in.data_ptr(),
@@ -79,6 +80,7 @@ def test_guards_untouched(gpu, name):
         assert guards_intact(ids_whole, g_ids, PAT32), f"{name}: a write landed next to the argmax ids"
         assert guards_intact(fl_whole, g_fl, PAT8), f"{name}: a write landed next to the argmax flags"
         assert guards_intact(ws_whole, g_ws, PAT8), f"{name}: a write landed next to the argmax workspace"
+        assert not ws_in.cpu().numpy().any(), f"{name}: the argmax workspace was not left zero"
         rids, rflags = oracle.argmax(w.logits)
         np.testing.assert_array_equal(ids_in.cpu().numpy(), rids)
         np.testing.assert_array_equal(fl_in.cpu().numpy(), rflags)

@@ -529,6 +529,33 @@ def _vocab_edge_rows(vocab, seed):
     return x
 
 
+def test_argmax_reuses_its_workspace(gpu):
+    # one zeroed workspace serves call after call: each leaves it zero, and
+    # the ids and flags stay bit-exact across rows of different lengths,
+    # nonfinite rows and ties across the 8192-logit chunks
+    import torch
+    rows, vocab = 40, 128000
+    x = _vocab_edge_rows(vocab, seed=61)
+    rng = np.random.Generator(np.random.PCG64(62))
+    x = np.concatenate([x, synth.normal_logits(rng, rows - x.shape[0], vocab)])
+    rids, rflags = oracle.argmax(x)
+    dev = gpu
+    xd = launch._dev(x, dev)
+    nbytes = binding.tf_argmax_workspace_bytes(rows, vocab)
+    ws = torch.zeros(nbytes // 8, dtype=torch.int64, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    for it in range(4):
+        ids = torch.full((rows,), -1, dtype=torch.int32, device=dev)
+        flags = torch.full((rows,), 7, dtype=torch.uint8, device=dev)
+        n = rows if it % 2 == 0 else rows // 2          # fewer rows on odd calls
+        assert binding.tf_argmax(xd.data_ptr(), n, vocab, vocab, ids.data_ptr(), flags.data_ptr(),
+                                 ws.data_ptr(), nbytes, st) == binding.TF_OK
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(ids.cpu().numpy()[:n], rids[:n])
+        np.testing.assert_array_equal(flags.cpu().numpy()[:n], rflags[:n])
+        assert not ws.cpu().numpy().any(), f"call {it} left the workspace dirty"
+
+
 @pytest.mark.parametrize("vocab", [1, 2, 7, 64, 255, 256, 257, 8191, 8192, 8193, 16384, 24577])
 def test_argmax_vocab_edges(gpu, vocab):
     print(f"argmax vocab {vocab}", flush=True)
