@@ -127,6 +127,24 @@ def test_rotated_grid_batched_equals_per_segment(gpu):
     assert dw.error_word() == 0
 
 
+def test_prompt_and_small_d256_shapes_agree_bitwise(gpu):
+    # head dim 256: a launch holding a segment of more than 64 query vectors
+    # per kv head runs every segment on the prompt shape (eight waves, 128
+    # vectors a workgroup); alone, the short segments take the small shape
+    # (four waves).  The bytes of every segment must agree (and the long one
+    # spans two query tiles).
+    keys = [3000, 260, 1400, 97]
+    w = synth.make_workload("wide", synth.KIND_PAGED, 16, 4, 256, [40, 3, 16, 1], keys, seed=61,
+                            page_size=32, pool_pages=sum(-(-k // 32) for k in keys) + 5, split_keys=512)
+    dw = launch.DeviceWorkload(w, gpu)
+    dw.run()
+    batched = dw.output()
+    assert np.array_equal(batched, dw.run_per_segment()), "D256: prompt and small shapes differ"
+    assert dw.error_word() == 0
+    ref = oracle.attn_workload(w)
+    assert_close(batched, ref, rel=REL_SMALL, what="D256 shapes", extra=weight_allowance(w, ref))
+
+
 @pytest.mark.parametrize("name", ["decode16", "verify8", "prompt512", "ring17"])
 def test_repeats_are_byte_identical(workloads, name):
     # five runs give the same bytes: the decode kernel (decode16) and the
