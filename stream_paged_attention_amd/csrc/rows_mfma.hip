@@ -74,8 +74,9 @@ struct MGeo {
     // LDS tile buffers (K and V): NBUF - 1 tiles in flight while one is
     // multiplied; 128 KB of LDS at D 256 (one workgroup of 8 waves a CU),
     // 64 KB for the small D 256 shape and D 64 (two workgroups of 4 waves),
-    // 48 KB at D 128 (three workgroups a CU: the ring drafter 25.7 -> 24.9 us
-    // against four buffers; six buffers, one workgroup a CU, 40 us)
+    // 48 KB at D 128 (room for three workgroups a CU; its ~170 registers a
+    // lane allow two: the ring drafter 25.7 -> 24.9 us against four buffers,
+    // 28.9 us with five, six buffers (one workgroup a CU) 40 us)
     static constexpr int NBUF = D == 256 ? (SMALL ? 2 : 4) : (D == 128 ? 3 : 8);
     static constexpr int PD = NBUF - 1;               // prefetch distance in tiles
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == TILE, "tile must split into 1 KB wave loads");
