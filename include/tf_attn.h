@@ -234,7 +234,7 @@ int tf_attn_static(const tf_attn_args *a, hipStream_t stream);
  * allocation serves every later call.  Calls that share a workspace must not
  * overlap.  Returns TF_E_INVALID for null pointers, vocab < 1, row_stride <
  * vocab; TF_E_WORKSPACE if the workspace is too small; TF_E_UNSUPPORTED for a
- * vocabulary of more than 65535 * 8192 logits.
+ * vocabulary of more than 65535 * 16384 logits.
  */
 int tf_argmax(const void *logits, int32_t n_rows, int32_t vocab, int64_t row_stride,
               int32_t *ids, uint8_t *flags, void *workspace, size_t workspace_bytes,

@@ -7,7 +7,7 @@
 // unsigned 16-bit rank (NaN taken as -inf, -0.0 as +0.0) above the complement
 // of its id, so the largest key is the largest value at the lowest id.  The
 // max of keys is order-independent, so the pick does not depend on how the
-// row is cut up.  One launch: one workgroup per (row, 8192-logit chunk)
+// row is cut up.  One launch: one workgroup per (row, 16384-logit chunk)
 // reduces its chunk to a key and a flag.  A row of one chunk is finished
 // there.  Otherwise each chunk folds its key into the row's 64-bit slot of
 // the workspace with an atomic max, then counts itself (and its flag) into
@@ -20,8 +20,8 @@ namespace tfa {
 
 namespace {
 
-constexpr int kChunk = 8192;
-constexpr int kThreads = 256;
+constexpr int kChunk = 16384;   // 8 chunks a row at 128 000 logits
+constexpr int kThreads = 512;
 constexpr int kPerThread = kChunk / kThreads;   // 32 logits, 4 groups of 8
 
 __device__ __forceinline__ uint32_t rank16(uint32_t b, uint32_t &nonfinite)

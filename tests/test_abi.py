@@ -241,8 +241,8 @@ def test_argmax_refusals():
     assert binding.tf_argmax(0x100, 2, 10, 10, 0x200, 0x300, 0x400, 1, 0) == binding.TF_E_WORKSPACE
     assert binding.tf_argmax(0, 0, 10, 10, 0, 0, 0, 0, 0) == binding.TF_OK   # no rows: nothing to do
     assert binding.tf_argmax_workspace_bytes(32, 128000) == 32 * 16     # one 16-byte slot a row
-    # a row's chunk count must fit 16 bits: at most 65535 chunks of 8192 logits
-    big = 65536 * 8192
+    # a row's chunk count must fit 16 bits: at most 65535 chunks of 16384 logits
+    big = 65536 * 16384
     assert binding.tf_argmax(0x100, 1, big, big, 0x200, 0x300, 0x400, 16, 0) == binding.TF_E_UNSUPPORTED
 
 

@@ -526,16 +526,19 @@ def test_argmax_small_cases(gpu):
     np.testing.assert_array_equal(flags2, rflags2)
 
 
+ARGMAX_CHUNK = 16384   # logits a workgroup of the argmax kernel reduces
+
+
 def _vocab_edge_rows(vocab, seed):
     """Rows for one vocabulary size: random, ties at both ends, across the
-    8192-logit chunk boundary and at the last chunk's first id, all equal,
+    kernel's chunk boundary and at the last chunk's first id, all equal,
     all NaN, and a +inf after a NaN."""
     rng = np.random.Generator(np.random.PCG64(seed))
     x = synth.normal_logits(rng, 8, vocab)
     synth.plant_tie(x, 1, sorted({0, vocab - 1}))
-    if vocab > 8192:
-        synth.plant_tie(x, 2, [8191, 8192])
-        last = (vocab - 1) // 8192 * 8192
+    if vocab > ARGMAX_CHUNK:
+        synth.plant_tie(x, 2, [ARGMAX_CHUNK - 1, ARGMAX_CHUNK])
+        last = (vocab - 1) // ARGMAX_CHUNK * ARGMAX_CHUNK
         synth.plant_tie(x, 3, sorted({5, last}))
     else:
         synth.plant_tie(x, 2, sorted({vocab // 2, vocab - 1}))
@@ -550,7 +553,7 @@ def _vocab_edge_rows(vocab, seed):
 def test_argmax_reuses_its_workspace(gpu):
     # one zeroed workspace serves call after call: each leaves it zero, and
     # the ids and flags stay bit-exact across rows of different lengths,
-    # nonfinite rows and ties across the 8192-logit chunks
+    # nonfinite rows and ties across the argmax chunks
     import torch
     rows, vocab = 40, 128000
     x = _vocab_edge_rows(vocab, seed=61)
@@ -574,7 +577,8 @@ def test_argmax_reuses_its_workspace(gpu):
         assert not ws.cpu().numpy().any(), f"call {it} left the workspace dirty"
 
 
-@pytest.mark.parametrize("vocab", [1, 2, 7, 64, 255, 256, 257, 8191, 8192, 8193, 16384, 24577])
+@pytest.mark.parametrize("vocab", [1, 2, 7, 64, 255, 256, 257, 8191, 8192, 8193, 16383, 16384, 16385,
+                                   24577, 40961])
 def test_argmax_vocab_edges(gpu, vocab):
     print(f"argmax vocab {vocab}", flush=True)
     x = _vocab_edge_rows(vocab, seed=vocab)
