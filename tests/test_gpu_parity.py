@@ -526,6 +526,32 @@ def test_argmax_small_cases(gpu):
     np.testing.assert_array_equal(flags2, rflags2)
 
 
+def test_argmax_scalar_loads(gpu):
+    # rows whose base is not 16-byte aligned (an odd row stride, or the whole
+    # buffer shifted by one element) take the element-by-element loads;
+    # several chunks a row, ties across the chunk boundary, nonfinite rows
+    import torch
+    vocab = 2 * 16384 + 77
+    x = _vocab_edge_rows(vocab, seed=71)
+    rids, rflags = oracle.argmax(x)
+    st = torch.cuda.current_stream(gpu).cuda_stream
+    rows = x.shape[0]
+    for stride, shift in ((vocab + 3, 0), (vocab, 1)):
+        buf = np.zeros((rows * stride + shift,), dtype=np.uint16)
+        for r in range(rows):
+            buf[shift + r * stride: shift + r * stride + vocab] = x[r]
+        xd = launch._dev(buf, gpu)
+        ids = torch.full((rows,), -1, dtype=torch.int32, device=gpu)
+        flags = torch.full((rows,), 7, dtype=torch.uint8, device=gpu)
+        nbytes = binding.tf_argmax_workspace_bytes(rows, vocab)
+        ws = torch.zeros(nbytes // 8, dtype=torch.int64, device=gpu)
+        assert binding.tf_argmax(xd.data_ptr() + 2 * shift, rows, vocab, stride, ids.data_ptr(),
+                                 flags.data_ptr(), ws.data_ptr(), nbytes, st) == binding.TF_OK
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(ids.cpu().numpy(), rids)
+        np.testing.assert_array_equal(flags.cpu().numpy(), rflags)
+
+
 ARGMAX_CHUNK = 16384   # logits a workgroup of the argmax kernel reduces
 
 
