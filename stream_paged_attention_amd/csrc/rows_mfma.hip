@@ -74,11 +74,15 @@ struct MGeo {
     // LDS tile buffers (K and V): NBUF - 1 tiles in flight while one is
     // multiplied; 128 KB of LDS at D 256 (one workgroup of 8 waves a CU),
     // 64 KB for the small D 256 shape and D 64 (two workgroups of 4 waves),
-    // 48 KB at D 128 (room for three workgroups a CU; its ~170 registers a
-    // lane allow two: the ring drafter 25.7 -> 24.9 us against four buffers,
-    // 28.9 us with five, six buffers (one workgroup a CU) 40 us)
+    // 48 KB used at D 128 (two workgroups a CU, see NBUF_LDS: the ring
+    // drafter 25.7 -> 24.9 us against four buffers, 28.9 us with five, six
+    // buffers (one workgroup a CU) 40 us)
     static constexpr int NBUF = D == 256 ? (SMALL ? 2 : 4) : (D == 128 ? 3 : 8);
     static constexpr int PD = NBUF - 1;               // prefetch distance in tiles
+    // LDS allocated: at D 128 four buffers' worth, of which three are used, so
+    // that two workgroups share a CU.  Three a CU (which the registers allow
+    // once they drop to 168) ran the ring drafter at 30.5 us against 26.5.
+    static constexpr int NBUF_LDS = D == 128 ? 4 : NBUF;
     static_assert(LOADS >= 1 && LOADS * NW * 1024 == TILE, "tile must split into 1 KB wave loads");
 };
 
@@ -156,7 +160,7 @@ __attribute__((amdgpu_waves_per_eu(SMALL ? 2 : 1))) void rows_mfma_kernel(RowsPa
     using G = MGeo<D, SMALL>;
     constexpr int KS = G::KS, DB = G::DB, NQB = G::NQB, QB = G::QB, LOADS = G::LOADS, NW = G::NW;
     constexpr int NBUF = G::NBUF, PD = G::PD;
-    __shared__ __attribute__((aligned(1024))) char kv_lds[NBUF][2][G::TILE];   // [buffer][K, V]
+    __shared__ __attribute__((aligned(1024))) char kv_lds[G::NBUF_LDS][2][G::TILE];   // [buffer][K, V]
 
     // ---- work item (grid_cell)
     const Cell cell = grid_cell(blockIdx.x, p.hkv, p.n_segments, p.n_split_max);
@@ -458,7 +462,30 @@ __attribute__((amdgpu_waves_per_eu(SMALL ? 2 : 1))) void rows_mfma_kernel(RowsPa
                             mx = max2(mx, x);
                         }
                 }
-                float a, bb;
+                tmax[b] = mx;   // the lane's own maximum; reduced below
+            }
+            // the weights from the current reference, rounded to bf16 (fp32
+            // sums: the value product and l take the same rounded weights).
+            // They are computed while the row maxima reduce across lanes; the
+            // rare step whose maximum moves the reference computes them again.
+            auto weights = [&]() {
+#pragma unroll
+                for (int b = 0; b < NQB; ++b) {
+                    float pe[8];
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            pe[kb * 4 + e] = exp2_fast(fmaf(s[b][kb][e], c, -mc[b]));
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        pf[b][w] = pack_bf16(pe[2 * w], pe[2 * w + 1]);
+                }
+            };
+            weights();
+#pragma unroll
+            for (int b = 0; b < NQB; ++b) {
+                float mx = tmax[b], a, bb;
                 swap16(mx, a, bb);
                 mx = max2(a, bb);
                 swap32(mx, a, bb);
@@ -479,22 +506,11 @@ __attribute__((amdgpu_waves_per_eu(SMALL ? 2 : 1))) void rows_mfma_kernel(RowsPa
                     for (int d = 0; d < DBG; ++d)
                         o[b][d] *= alpha;
                 }
+                weights();
             }
 #pragma unroll
-            for (int b = 0; b < NQB; ++b) {
-                float pe[8];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        pe[kb * 4 + e] = exp2_fast(fmaf(s[b][kb][e], c, -mc[b]));
-                // the weights rounded to bf16 (fp32 sums): the value product and
-                // l take the same rounded weights
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    pf[b][w] = pack_bf16(pe[2 * w], pe[2 * w + 1]);
+            for (int b = 0; b < NQB; ++b)
                 lsum[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, as_bf16x8(pf[b]), lsum[b], 0, 0, 0);
-            }
 
             // -- values: O^T += V^T P^T per 16-dim block.  V^T fragment of lane
             // (lg, lc): dims 16 db + lc, keys 4 lg .. + 4 and 16 + 4 lg .. + 4,
