@@ -81,3 +81,16 @@ def test_rows_kernels_use_no_scratch_and_the_small_shape_fits_two_a_cu(tmp_path)
                 assert d[".amdhsa_next_free_vgpr"] <= 256, name
                 assert d[".amdhsa_group_segment_fixed_size"] <= 80 * 1024, name
     assert small == 9   # 3 storage kinds x 3 masks
+
+
+def test_d128_matrix_core_kernel_runs_two_workgroups_a_cu(tmp_path):
+    # three workgroups a CU ran the ring drafter 15 % slower than two: the
+    # D 128 kernel allocates more than a third of a CU's 160 KB of LDS
+    desc = _descriptors(_asm("rows_mfma.hip", tmp_path))
+    n = 0
+    for name, d in desc.items():
+        if "rows_mfma_kernelILi128" in name:
+            n += 1
+            assert d[".amdhsa_group_segment_fixed_size"] > 160 * 1024 // 3, name
+            assert d[".amdhsa_group_segment_fixed_size"] <= 160 * 1024 // 2, name
+    assert n == 9
