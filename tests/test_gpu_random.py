@@ -64,3 +64,31 @@ def test_random_shape(gpu, i):
     assert_close(got, ref, rel=REL_SMALL, what=f"random {i}", extra=weight_allowance(w, ref))
     assert dw.error_word() == 0
     assert np.array_equal(got, dw.run_per_segment()), f"random {i}: batched differs from per-segment"
+
+
+def test_many_streams_in_one_launch(gpu):
+    # 256 decode streams of 1 to 2048 keys in one launch (grid size, partial
+    # record offsets, the page list of every stream), against the oracle
+    rng = np.random.Generator(np.random.PCG64(77))
+    keys = [int(k) for k in rng.integers(1, 2049, size=256)]
+    w = synth.make_workload("many", synth.KIND_PAGED, 16, 4, 128, [1] * 256, keys, seed=78,
+                            page_size=32, pool_pages=sum(-(-k // 32) for k in keys) + 9, split_keys=256)
+    dw = launch.DeviceWorkload(w, gpu)
+    assert dw.check_table() == binding.TF_OK
+    dw.run()
+    ref = oracle.attn_workload(w)
+    assert_close(dw.output(), ref, rel=REL_SMALL, what="many streams", extra=weight_allowance(w, ref))
+    assert dw.error_word() == 0
+
+
+def test_long_prompt_chunk(gpu):
+    # one 1024-row prompt chunk at head dim 128 (32 query tiles per kv head,
+    # causal over 1500 committed keys), against the oracle
+    w = synth.make_workload("long", synth.KIND_PAGED, 16, 4, 128, [1024], [2524], seed=79,
+                            page_size=64, pool_pages=45, split_keys=512)
+    dw = launch.DeviceWorkload(w, gpu)
+    assert dw.check_table() == binding.TF_OK
+    dw.run()
+    ref = oracle.attn_workload(w)
+    assert_close(dw.output(), ref, rel=REL_SMALL, what="long prompt", extra=weight_allowance(w, ref))
+    assert dw.error_word() == 0
