@@ -21,8 +21,8 @@ namespace tfa {
 namespace {
 
 constexpr int kChunk = 16384;   // 8 chunks a row at 128 000 logits
-constexpr int kThreads = 512;
-constexpr int kPerThread = kChunk / kThreads;   // 32 logits, 4 groups of 8
+constexpr int kThreads = 1024;
+constexpr int kPerThread = kChunk / kThreads;   // 16 logits, 2 groups of 8
 
 __device__ __forceinline__ uint32_t rank16(uint32_t b, uint32_t &nonfinite)
 {
