@@ -174,7 +174,12 @@ __attribute__((amdgpu_waves_per_eu(SMALL ? 2 : 1))) void rows_mfma_kernel(RowsPa
     const int lg = lane >> 4;     // lane group (0..3)
     const int lc = lane & 15;     // lane column
 
-    const tf_segment &sd = p.segs[seg_i];
+    // the whole row in scalar registers here, in one memory round trip (a
+    // copy, so the checks below read registers): left to the compiler, each
+    // field was fetched at its first use, one wait after another
+    const tf_segment sd = p.segs[seg_i];
+    asm volatile("" ::"s"(sd.k), "s"(sd.v), "s"(sd.pages), "s"(sd.capacity), "s"(sd.first), "s"(sd.row_offset),
+                 "s"(sd.n_rows), "s"(sd.key_count), "s"(sd.partial_offset));
     const char *kbase = static_cast<const char *>(sd.k);
     const char *vbase = static_cast<const char *>(sd.v);
     const int32_t *pages = sd.pages;

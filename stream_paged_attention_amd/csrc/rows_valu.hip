@@ -472,7 +472,12 @@ __global__ __launch_bounds__(kThreads) void rows_valu_kernel(RowsParams p)
     const int delta = odd ? -1 : 1;
     const uint32_t lane_v = G::PAIR ? pair_lane_bytes<D, QT>(sl, odd) : 0u;
 
-    const tf_segment &sd = p.segs[seg_i];
+    // the whole row in scalar registers here, in one memory round trip (a
+    // copy, so the checks below read registers): left to the compiler, each
+    // field was fetched at its first use, one wait after another
+    const tf_segment sd = p.segs[seg_i];
+    asm volatile("" ::"s"(sd.k), "s"(sd.v), "s"(sd.pages), "s"(sd.capacity), "s"(sd.first), "s"(sd.row_offset),
+                 "s"(sd.n_rows), "s"(sd.key_count), "s"(sd.partial_offset));
     Seg s;
     s.k = static_cast<const uint16_t *>(sd.k);
     s.v = static_cast<const uint16_t *>(sd.v);
