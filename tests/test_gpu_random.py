@@ -92,3 +92,70 @@ def test_long_prompt_chunk(gpu):
     ref = oracle.attn_workload(w)
     assert_close(dw.output(), ref, rel=REL_SMALL, what="long prompt", extra=weight_allowance(w, ref))
     assert dw.error_word() == 0
+
+
+ARGMAX_CASES = 40
+
+
+def _argmax_case(i):
+    """Rows, vocabulary, row stride, base shift and plants of one seeded case."""
+    rng = np.random.Generator(np.random.PCG64(5000 + i))
+    rows = int(rng.integers(1, 41))
+    vocab = int(np.exp(rng.uniform(0.0, np.log(200_000))))
+    vocab = max(1, vocab)
+    pad = int(rng.integers(0, 9))          # row stride = vocab + pad
+    shift = int(rng.integers(0, 2))        # 1: the buffer starts one element past 16-byte alignment
+    return rows, vocab, pad, shift, int(rng.integers(0, 1 << 30))
+
+
+def _argmax_rows(rows, vocab, seed):
+    """Random bf16 logits with plants: ties across the kernel's chunk
+    boundaries and at both ends, NaN and +-Inf, all-equal rows."""
+    from tests.test_gpu_parity import ARGMAX_CHUNK
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = synth.normal_logits(rng, rows, vocab)
+    for r in range(rows):
+        kind = int(rng.integers(0, 8))
+        if kind == 0 and vocab > 1:
+            bounds = [b for b in range(ARGMAX_CHUNK, vocab, ARGMAX_CHUNK)]
+            ids = sorted({int(rng.integers(0, vocab)), (bounds[-1] if bounds else vocab - 1)})
+            synth.plant_tie(x, r, ids)
+        elif kind == 1:
+            synth.plant_tie(x, r, sorted({0, vocab - 1}))
+        elif kind == 2:
+            x[r, int(rng.integers(0, vocab))] = synth.BF16_NAN
+        elif kind == 3:
+            x[r, int(rng.integers(0, vocab))] = synth.BF16_POS_INF
+            x[r, int(rng.integers(0, vocab))] = synth.BF16_NAN
+        elif kind == 4:
+            x[r, :] = synth.BF16_NEG_INF
+        elif kind == 5:
+            x[r, :] = synth.f32_to_bf16_bits(np.float32(rng.normal()))
+    return x
+
+
+@pytest.mark.parametrize("i", range(ARGMAX_CASES))
+def test_random_argmax(gpu, i):
+    # one launch over rows of a random vocabulary and stride, aligned or not:
+    # ids and flags bit-exact against the oracle, the workspace left zero
+    import torch
+    rows, vocab, pad, shift, seed = _argmax_case(i)
+    print(f"random argmax {i}: rows {rows} vocab {vocab} stride +{pad} shift {shift}", flush=True)
+    x = _argmax_rows(rows, vocab, seed)
+    rids, rflags = oracle.argmax(x)
+    stride = vocab + pad
+    buf = np.zeros((rows * stride + shift,), dtype=np.uint16)
+    for r in range(rows):
+        buf[shift + r * stride: shift + r * stride + vocab] = x[r]
+    xd = launch._dev(buf, gpu)
+    ids = torch.full((rows,), -7, dtype=torch.int32, device=gpu)
+    flags = torch.full((rows,), 9, dtype=torch.uint8, device=gpu)
+    nbytes = binding.tf_argmax_workspace_bytes(rows, vocab)
+    ws = torch.zeros(max(nbytes, 8) // 8, dtype=torch.int64, device=gpu)
+    st = torch.cuda.current_stream(gpu).cuda_stream
+    assert binding.tf_argmax(xd.data_ptr() + 2 * shift, rows, vocab, stride, ids.data_ptr(),
+                             flags.data_ptr(), ws.data_ptr(), nbytes, st) == binding.TF_OK
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), rids)
+    np.testing.assert_array_equal(flags.cpu().numpy(), rflags)
+    assert not ws.cpu().numpy().any(), f"random argmax {i}: workspace left dirty"
