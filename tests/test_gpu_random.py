@@ -159,3 +159,93 @@ def test_random_argmax(gpu, i):
     np.testing.assert_array_equal(ids.cpu().numpy(), rids)
     np.testing.assert_array_equal(flags.cpu().numpy(), rflags)
     assert not ws.cpu().numpy().any(), f"random argmax {i}: workspace left dirty"
+
+
+PUT_CASES = 24
+
+
+def _put_workload(i):
+    """A seeded round for tf_kv_put: storage kind, head dim, heads, page size,
+    ring heads (wrapping or not), ragged segments of 1-20 new rows."""
+    rng = np.random.Generator(np.random.PCG64(7000 + i))
+    kind = ["paged", "ring", "contig"][int(rng.integers(0, 3))]
+    d = [64, 128, 256][int(rng.integers(0, 3))]
+    hq, hkv = HEADS[int(rng.integers(0, len(HEADS)))]
+    n_seg = int(rng.integers(1, 6))
+    rows = [int(rng.integers(1, 21)) for _ in range(n_seg)]
+    cap = max(64, 1_500_000 // (hq * d))
+    keys = [int(rng.integers(r, max(r, cap) + 1)) for r in rows]
+    page = [32, 64, 128, 256, 512, 1024][int(rng.integers(0, 6))]
+    seed = int(rng.integers(0, 1 << 30))
+    if kind == "paged":
+        kw = dict(page_size=page, pool_pages=sum(-(-k // page) for k in keys) + int(rng.integers(1, 6)))
+    elif kind == "ring":
+        slots = [k + int(rng.integers(0, 40)) for k in keys]
+        kw = dict(ring_slots=slots, ring_heads=[int(rng.integers(0, s)) for s in slots])
+    else:
+        kw = dict(contig_capacity=[k + int(rng.integers(0, 40)) for k in keys])
+    w = synth.make_workload(f"put{i}", kind, hq, hkv, d, rows, keys, seed=seed, split_keys=64, **kw)
+    return w, page
+
+
+@pytest.mark.parametrize("i", range(PUT_CASES))
+def test_random_put(gpu, i):
+    # the round's new rows appended by tf_kv_put: storage bit-exact against the
+    # reference append, no error bit, and attention after the put byte-equal
+    # to attention over the same keys placed beforehand
+    from tests.kv_put_cases import oracle_after, round_inputs
+    w, page = _put_workload(i)
+    print(f"random put {i}: {w.kind} D{w.head_dim} {w.n_q_heads}/{w.n_kv_heads} "
+          f"rows {[s.n_rows for s in w.segments]} keys {[s.key_count for s in w.segments]} P{page}", flush=True)
+    before, k_new, v_new = round_inputs(w)
+    dw = launch.DeviceWorkload(before, gpu)
+    dw.kv_put(k_new, v_new)
+    assert dw.error_word() == 0
+    ek, ev = oracle_after(before, k_new, v_new)
+    k, v = dw.storage()
+    if w.kind == "paged":
+        assert np.array_equal(k, ek) and np.array_equal(v, ev)
+    else:
+        assert all(np.array_equal(a, b) for a, b in zip(k, ek))
+        assert all(np.array_equal(a, b) for a, b in zip(v, ev))
+    dw.run()
+    ref = launch.DeviceWorkload(w, gpu)
+    ref.run()
+    assert np.array_equal(dw.output(), ref.output()), f"random put {i}: attention after the put differs"
+
+
+STATE_CASES = 16
+
+
+@pytest.mark.parametrize("i", range(STATE_CASES))
+def test_random_state_copy(gpu, i):
+    # tf_state_save then tf_state_restore into fresh pages of the same pool:
+    # every byte as the reference gives it (the pool untouched by the save,
+    # the rows past `at` and the other pages untouched by the restore)
+    from oracle import state_copy
+    from tests.state_cases import layers_case
+    rng = np.random.Generator(np.random.PCG64(9000 + i))
+    layers = int(rng.integers(1, 5))
+    hkv = [1, 2, 4, 8][int(rng.integers(0, 4))]
+    d = [64, 128, 256][int(rng.integers(0, 3))]
+    page = [32, 64, 128, 256, 512, 1024][int(rng.integers(0, 6))]
+    at = int(rng.integers(1, max(2, 400_000 // (hkv * d)) + 1))
+    print(f"random state {i}: {layers} layers, Hkv {hkv}, D{d}, P{page}, at {at}", flush=True)
+    case = layers_case(seed=int(rng.integers(0, 1 << 30)), n_layers=layers, hkv=hkv, d=d, page_size=page, at=at)
+    ds = launch.DeviceState(case.pools, case.states, case.pages, at, gpu)
+    ds.save()
+    pools, states = ds.host()
+    ref_states = state_copy.save(case.pools, case.pages, at, case.states)
+    for (gk, gv), (rk, rv) in zip(states, ref_states):
+        assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
+    for (gk, gv), (rk, rv) in zip(pools, case.pools):
+        assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
+    free = np.setdiff1d(np.arange(case.pool_pages), case.pages)
+    new_pages = rng.choice(free, size=len(case.pages), replace=False).astype(np.int32)
+    ds.set_pages(new_pages)
+    ds.restore()
+    pools2, _ = ds.host()
+    ref_pools = state_copy.restore(ref_states, new_pages, at, case.pools)
+    for (gk, gv), (rk, rv) in zip(pools2, ref_pools):
+        assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
+    assert ds.error_word() == 0
